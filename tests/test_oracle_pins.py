@@ -1,0 +1,441 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Page: "GPU Performance of an Entropy-Stable Discontinuous Galerkin Euler
+Solver with Non-Conservative Terms" (arXiv 2605.16684v2), [ESDG-GPU].
+
+  consistency F(q,q) = physical flux ........... Eq. 1 and Eq. 4 of [ESDG-GPU]
+  symmetry of the conservative part ............ [ESDG-GPU §4.1] (S and the density/energy
+                                                  components are symmetric)
+  gravity partner scaling G -> -G b-/b+ ........ [ESDG-GPU §4.1]
+  pairwise entropy condition ................... entropy conservation of the volume flux
+                                                  [ESDG-GPU §3]; derived
+  element entropy identity ..................... same, summed with SBP
+  free stream on curved meshes ................. closed form of Eq. 2 at constant state
+  isothermal hydrostatic balance ............... closed form of Eq. 2 (derived)
+  Cartesian reduction .......................... Eq. 2 on an affine axis-aligned element
+  50-digit brute force ......................... independent arbitrary-precision evaluation
+"""
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import inputs as I
+
+G = I.GAMMA
+
+
+# --- helpers (independent of the oracle) ----------------------------------
+def random_prims(rng, n, phi_range=(0.0, 1.0e4)):
+    rho = rng.uniform(0.5, 1.5, n)
+    u = rng.uniform(-50.0, 50.0, (3, n))
+    p = rng.uniform(0.5e5, 1.5e5, n)
+    phi = rng.uniform(*phi_range, n)
+    return rho, u, p, phi
+
+
+def cons(rho, u, p, phi):
+    return I.conserved(rho, u, p, phi).T.copy()  # [n][5]
+
+
+def physical_flux(rho, u, p, E, j):
+    """f_j of Eq. 1: (rho u_j, rho u_j u_m + p delta_jm, (E + p) u_j)."""
+    f = np.empty((rho.size, 5))
+    f[:, 0] = rho * u[j]
+    for m in range(3):
+        f[:, 1 + m] = rho * u[j] * u[m] + (p if m == j else 0.0)
+    f[:, 4] = (E + p) * u[j]
+    return f
+
+
+def entropy_vars(rho, u, p, phi):
+    """v = d eta/dq for eta = -rho s/(gamma-1), s = ln p - gamma ln rho, with
+    p = (gamma-1)(E - |m|^2/(2rho) - rho phi):
+    v = ((gamma-s)/(gamma-1) - b|u|^2 + 2 b phi, 2 b u, -2 b), b = rho/(2p)."""
+    s = np.log(p) - G * np.log(rho)
+    b = rho / (2 * p)
+    usq = (u ** 2).sum(0)
+    return np.stack([(G - s) / (G - 1) - b * usq + 2 * b * phi, 2 * b * u[0], 2 * b * u[1],
+                     2 * b * u[2], -2 * b]).T
+
+
+# --- two-point flux -------------------------------------------------------
+def check_consistency(orc, j):
+    rng = np.random.default_rng(10 + j)
+    rho, u, p, phi = random_prims(rng, 500)
+    q = cons(rho, u, p, phi)
+    F = orc.ec_flux(q, phi, q, phi, j)
+    f = physical_flux(rho, u, p, q[:, 4], j)
+    scale = np.abs(f).max(0)
+    assert np.all(np.abs(F - f).max(0) <= 1e-14 * scale)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_consistency(j):
+    check_consistency(oracle.default(), j)
+
+
+def check_symmetry_of_conservative_part(orc, j):
+    rng = np.random.default_rng(20 + j)
+    rho_i, u_i, p_i, phi_i = random_prims(rng, 300)
+    rho_l, u_l, p_l, phi_l = random_prims(rng, 300)
+    qi, ql = cons(rho_i, u_i, p_i, phi_i), cons(rho_l, u_l, p_l, phi_l)
+    Fil = orc.ec_flux(qi, phi_i, ql, phi_l, j)
+    Fli = orc.ec_flux(ql, phi_l, qi, phi_i, j)
+    # density and energy are symmetric for any geopotential
+    for f in (0, 4):
+        np.testing.assert_allclose(Fil[:, f], Fli[:, f], rtol=1e-13, atol=1e-13 * np.abs(Fil[:, f]).max())
+    # with a common geopotential the whole flux is symmetric
+    qi0, ql0 = cons(rho_i, u_i, p_i, phi_i), cons(rho_l, u_l, p_l, phi_i)
+    A = orc.ec_flux(qi0, phi_i, ql0, phi_i, j)
+    B = orc.ec_flux(ql0, phi_i, qi0, phi_i, j)
+    np.testing.assert_allclose(A, B, rtol=1e-13, atol=1e-13 * np.abs(A).max())
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_symmetry_of_conservative_part(j):
+    check_symmetry_of_conservative_part(oracle.default(), j)
+
+
+def check_gravity_partner_scaling(orc, j):
+    """Gravity part G = F(phi_i, phi_l) - F(phi, phi) at fixed (rho, u, p): only
+    the j-th momentum component, and G(l, i) = -G(i, l) b_i / b_l."""
+    rng = np.random.default_rng(30 + j)
+    rho_i, u_i, p_i, phi_i = random_prims(rng, 300)
+    rho_l, u_l, p_l, phi_l = random_prims(rng, 300)
+    zero = np.zeros(300)
+    Fil = orc.ec_flux(cons(rho_i, u_i, p_i, phi_i), phi_i, cons(rho_l, u_l, p_l, phi_l), phi_l, j)
+    Fli = orc.ec_flux(cons(rho_l, u_l, p_l, phi_l), phi_l, cons(rho_i, u_i, p_i, phi_i), phi_i, j)
+    S = orc.ec_flux(cons(rho_i, u_i, p_i, zero), zero, cons(rho_l, u_l, p_l, zero), zero, j)
+    Gil, Gli = Fil - S, Fli - S
+    for m in range(3):
+        if m != j:
+            assert np.abs(Gil[:, 1 + m]).max() <= 1e-9 * np.abs(S[:, 1 + m]).max()
+    b_i, b_l = rho_i / (2 * p_i), rho_l / (2 * p_l)
+    g = Gil[:, 1 + j]
+    assert np.abs(g).min() > 0
+    np.testing.assert_allclose(Gli[:, 1 + j], -g * b_i / b_l, rtol=1e-7, atol=1e-9 * np.abs(g).max())
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_gravity_partner_scaling(j):
+    check_gravity_partner_scaling(oracle.default(), j)
+
+
+def check_pairwise_entropy_condition(orc, j):
+    """v_i . F_j(q_i, q_l) - v_l . F_j(q_l, q_i) = psi_j(i) - psi_j(l), psi_j = rho u_j."""
+    rng = np.random.default_rng(40 + j)
+    rho_i, u_i, p_i, phi_i = random_prims(rng, 1000)
+    rho_l, u_l, p_l, phi_l = random_prims(rng, 1000)
+    qi, ql = cons(rho_i, u_i, p_i, phi_i), cons(rho_l, u_l, p_l, phi_l)
+    Fil = orc.ec_flux(qi, phi_i, ql, phi_l, j)
+    Fli = orc.ec_flux(ql, phi_l, qi, phi_i, j)
+    vi, vl = entropy_vars(rho_i, u_i, p_i, phi_i), entropy_vars(rho_l, u_l, p_l, phi_l)
+    lhs = (vi * Fil).sum(1) - (vl * Fli).sum(1)
+    rhs = rho_i * u_i[j] - rho_l * u_l[j]
+    # terms of v.F are O(|v| |F|) ~ 1e2..1e3 each; round-off is ~1e-16 of that
+    scale = (np.abs(vi * Fil).sum(1) + np.abs(vl * Fli).sum(1))
+    assert np.all(np.abs(lhs - rhs) <= 1e-13 * scale)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_pairwise_entropy_condition(j):
+    check_pairwise_entropy_condition(oracle.default(), j)
+
+
+def check_flux_nearly_equal_states(orc):
+    """The log mean's limit: as q_l -> q_i the flux tends to the physical flux
+    smoothly (no cancellation blow-up)."""
+    rng = np.random.default_rng(5)
+    rho, u, p, phi = random_prims(rng, 200)
+    for eps in (1e-3, 1e-6, 1e-9, 1e-12):
+        rho_l = rho * (1 + eps * rng.uniform(-1, 1, 200))
+        p_l = p * (1 + eps * rng.uniform(-1, 1, 200))
+        qi, ql = cons(rho, u, p, phi), cons(rho_l, u, p_l, phi)
+        F = orc.ec_flux(qi, phi, ql, phi, 2)
+        f = physical_flux(rho, u, p, qi[:, 4], 2)
+        assert np.all(np.abs(F - f).max(0) <= 20 * eps * np.abs(f).max(0) + 1e-13 * np.abs(f).max(0))
+
+
+def test_flux_nearly_equal_states():
+    check_flux_nearly_equal_states(oracle.default())
+
+
+# --- arbitrary-precision brute force ----------------------------------------
+mpmath.mp.dps = 50
+
+
+def mp_flux(qi, phii, ql, phil, j):
+    """Straight transcription of the two-point flux at 50 digits (same reading
+    as the oracle), evaluated with mpmath's own log."""
+    mp = mpmath.mpf
+    def prim(q, phi):
+        rho = mp(q[0]); u = [mp(q[1]) / rho, mp(q[2]) / rho, mp(q[3]) / rho]
+        p = (mp(G) - 1) * (mp(q[4]) - (mp(q[1]) ** 2 + mp(q[2]) ** 2 + mp(q[3]) ** 2) / (2 * rho) - rho * mp(phi))
+        return rho, u, p, rho / (2 * p), mp(phi)
+    ri, ui, pi_, bi, fi = prim(qi, phii)
+    rl, ul, pl, bl, fl = prim(ql, phil)
+    lm = lambda a, c: a if a == c else (c - a) / (mpmath.log(c) - mpmath.log(a))
+    ra, rlog = (ri + rl) / 2, lm(ri, rl)
+    ba, blog = (bi + bl) / 2, lm(bi, bl)
+    ua = [(ui[m] + ul[m]) / 2 for m in range(3)]
+    usq = ((ui[0] ** 2 + ui[1] ** 2 + ui[2] ** 2) + (ul[0] ** 2 + ul[1] ** 2 + ul[2] ** 2)) / 2
+    Fr = rlog * ua[j]
+    pt = ra / (2 * ba)
+    rhat = ba * rlog / bi
+    F = [Fr] + [Fr * ua[m] + ((pt + rhat * (fl - fi) / 2) if m == j else 0) for m in range(3)]
+    FE = (1 / (2 * (mp(G) - 1) * blog) - usq / 2 + (fi + fl) / 2) * Fr
+    FE += sum(ua[m] * (Fr * ua[m] + (pt if m == j else 0)) for m in range(3))
+    return F + [FE]
+
+
+def check_flux_vs_50_digits(orc):
+    rng = np.random.default_rng(6)
+    rho_i, u_i, p_i, phi_i = random_prims(rng, 40)
+    rho_l, u_l, p_l, phi_l = random_prims(rng, 40)
+    # make some pairs nearly equal, where the log mean is ill-conditioned
+    rho_l[:10] = rho_i[:10] * (1 + 1e-9)
+    p_l[:10] = p_i[:10] * (1 - 3e-10)
+    qi, ql = cons(rho_i, u_i, p_i, phi_i), cons(rho_l, u_l, p_l, phi_l)
+    for j in range(3):
+        F = orc.ec_flux(qi, phi_i, ql, phi_l, j)
+        for n in range(40):
+            ref = np.array([float(x) for x in mp_flux(qi[n], phi_i[n], ql[n], phi_l[n], j)])
+            assert np.all(np.abs(F[n] - ref) <= 1e-13 * np.abs(ref).max())
+
+
+def test_flux_vs_50_digits():
+    check_flux_vs_50_digits(oracle.default())
+
+
+def mp_volume_rhs(q, phi, geom, D, N):
+    """Volume term of one element at 50 digits, every ordered pair."""
+    Nq = N + 1
+    Np = Nq ** 3
+    out = np.empty((5, Np))
+    for c in range(Nq):
+        for b in range(Nq):
+            for a in range(Nq):
+                i = a + Nq * (b + Nq * c)
+                acc = [mpmath.mpf(0)] * 5
+                for k in range(3):
+                    ik = (a, b, c)[k]
+                    for l in range(Nq):
+                        if l == ik:
+                            continue
+                        il = [l + Nq * (b + Nq * c), a + Nq * (l + Nq * c), a + Nq * (b + Nq * l)][k]
+                        for j in range(3):
+                            nj = mpmath.mpf(geom[3 * k + j, i]) + mpmath.mpf(geom[3 * k + j, il])
+                            F = mp_flux(q[:, i], phi[i], q[:, il], phi[il], j)
+                            for f in range(5):
+                                acc[f] += mpmath.mpf(D[ik, l]) * nj * F[f]
+                for f in range(5):
+                    out[f, i] = float(-acc[f] / mpmath.mpf(geom[9, i]))
+    return out
+
+
+def check_element_vs_50_digits(orc, N):
+    """One element with random state and random (not mapping-derived) metrics."""
+    rng = np.random.default_rng(60 + N)
+    Np = (N + 1) ** 3
+    rho, u, p, phi = random_prims(rng, Np)
+    q = cons(rho, u, p, phi).T.copy()
+    geom = rng.uniform(-1.0, 1.0, (10, Np))
+    geom[9] = rng.uniform(0.5, 2.0, Np)
+    D = I.diff_matrix(N)
+    ref = mp_volume_rhs(q, phi, geom, D, N)
+    got = orc.volume_rhs(q[:, None, :], phi[None, :], geom[:, None, :], D, N)[:, 0, :]
+    for f in range(5):
+        assert np.abs(got[f] - ref[f]).max() <= 1e-13 * np.abs(ref[f]).max()
+
+
+@pytest.mark.parametrize("N", [1, 2])
+def test_element_vs_50_digits(N):
+    check_element_vs_50_digits(oracle.default(), N)
+
+
+# --- element identities -----------------------------------------------------
+def weights3(N):
+    _, w = I.lgl(N)
+    return np.einsum("c,b,a->cba", w, w, w).ravel(), w
+
+
+def dterm(D, geom_e, N):
+    """(sum_k D^k Ja^k_j)(i) for each j, one element: [3][Np]."""
+    Nq = N + 1
+    g = geom_e.reshape(10, Nq, Nq, Nq)
+    return np.stack([(I._apply_d(D, g[j], 0) + I._apply_d(D, g[3 + j], 1)
+                      + I._apply_d(D, g[6 + j], 2)).ravel() for j in range(3)])
+
+
+def diag_term(D, geom_e, N):
+    """sum_k D[i_k][i_k] Ja^k_j(i), one element: [3][Np]."""
+    Nq = N + 1
+    dd = np.diag(D)
+    c, b, a = np.meshgrid(range(Nq), range(Nq), range(Nq), indexing="ij")
+    c, b, a = c.ravel(), b.ravel(), a.ravel()
+    return np.stack([dd[a] * geom_e[j] + dd[b] * geom_e[3 + j] + dd[c] * geom_e[6 + j]
+                     for j in range(3)])
+
+
+def smooth_state(X, rng):
+    x, y, z = X
+    k = rng.uniform(1.0, 3.0, 6)
+    rho = 1.0 + 0.3 * np.sin(k[0] * x + k[1] * y) * np.cos(k[2] * z)
+    u = np.stack([30 * np.sin(k[3] * y + z), 20 * np.cos(k[4] * x - y), 10 * np.sin(k[5] * z + x)])
+    p = 1e5 * (1 + 0.2 * np.cos(k[1] * x + k[2] * z))
+    phi = I.GRAV * 1000.0 * (z + 0.1 * np.sin(3 * x))
+    return rho, u, p, phi
+
+
+def check_element_entropy_identity(orc, N, random_metrics):
+    """sum_i w_i J_i v_i . rhs_i = sum_k face-sum w_face [(Ja^k . psi)|_{+1} - (Ja^k . psi)|_{-1}]
+    - sum_i w_i sum_j psi_j (sum_k D^k Ja^k_j)(i), for any metrics (derived from
+    the pairwise entropy condition and summation by parts)."""
+    rng = np.random.default_rng(70 + N)
+    D = I.diff_matrix(N)
+    Nq = N + 1
+    X = I.box_mesh((2, 1, 1), (0, 0, 0), (2, 1, 1), N, warp_frac=0.05, seed=N,
+                   warp_wavelength=(1, 1, 1))
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    Xf = X.reshape(3, ne, -1)
+    if random_metrics:
+        geom[:9] = rng.uniform(-1, 1, geom[:9].shape)
+    rho, u, p, phi = smooth_state(Xf, rng)
+    q = I.conserved(rho, u, p, phi)
+    rhs = orc.volume_rhs(q, phi, geom, D, N)
+    W, w = weights3(N)
+    for e in range(ne):
+        v = entropy_vars(rho[e], u[:, e], p[e], phi[e])  # [Np][5]
+        J = geom[9, e]
+        lhs_terms = W[:, None] * J[:, None] * v * rhs[:, e, :].T
+        lhs = lhs_terms.sum()
+        psi = rho[e] * u[:, e]  # [3][Np]
+        g = geom[:, e, :].reshape(10, Nq, Nq, Nq)
+        ps = psi.reshape(3, Nq, Nq, Nq)
+        bnd = 0.0
+        for k in range(3):
+            contra = sum(g[3 * k + j] * ps[j] for j in range(3))  # Ja^k . psi
+            if k == 0:
+                bnd += np.einsum("c,b,cb->", w, w, contra[:, :, -1] - contra[:, :, 0])
+            elif k == 1:
+                bnd += np.einsum("c,a,ca->", w, w, contra[:, -1, :] - contra[:, 0, :])
+            else:
+                bnd += np.einsum("b,a,ba->", w, w, contra[-1, :, :] - contra[0, :, :])
+        resid = (W * (psi * dterm(D, geom[:, e, :], N)).sum(0)).sum()
+        scale = np.abs(lhs_terms).sum()
+        assert abs(lhs - (bnd - resid)) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("N,random_metrics", [(2, True), (3, False), (4, True), (4, False), (7, False)])
+def test_element_entropy_identity(N, random_metrics):
+    check_element_entropy_identity(oracle.default(), N, random_metrics)
+
+
+def check_free_stream(orc, N):
+    """Constant state and geopotential on a curved mesh:
+    rhs_i = -(1/J_i) sum_j [ (sum_k D^k Ja^k_j)(i) - 2 sum_k D[i_k][i_k] Ja^k_j(i) ] f_j(q),
+    zero at interior nodes (metric identities)."""
+    D = I.diff_matrix(N)
+    X = I.box_mesh((2, 2, 1), (0, 0, 0), (2, 2, 1), N, warp_frac=0.05, seed=N,
+                   warp_wavelength=(1, 1, 1))
+    geom = I.metrics(X, D)
+    ne, Np = X.shape[1], (N + 1) ** 3
+    rho, u, p, phi = 1.2, np.array([10.0, -5.0, 3.0]), 9.0e4, 500.0
+    q1 = I.conserved(np.array(rho), u, np.array(p), np.array(phi))
+    q = np.broadcast_to(q1[:, None, None], (5, ne, Np)).copy()
+    phis = np.full((ne, Np), phi)
+    rhs = orc.volume_rhs(q, phis, geom, D, N)
+    E = q1[4]
+    f = [physical_flux(np.array([rho]), u[:, None], np.array([p]), np.array([E]), j)[0] for j in range(3)]
+    for e in range(ne):
+        dt, dg = dterm(D, geom[:, e], N), diag_term(D, geom[:, e], N)
+        expect = -sum(np.outer(f[j], dt[j] - 2 * dg[j]) for j in range(3)) / geom[9, e]
+        scale = np.abs(expect).max(1)
+        assert np.all(np.abs(rhs[:, e, :] - expect).max(1) <= 1e-12 * scale + 1e-30)
+        # interior nodes: zero to round-off relative to the face values
+        idx = np.arange(N + 1)
+        inner = (idx > 0) & (idx < N)
+        interior = np.einsum("c,b,a->cba", inner, inner, inner).ravel()
+        assert np.abs(rhs[:, e, interior]).max() <= 1e-11 * np.abs(rhs[:, e]).max()
+
+
+@pytest.mark.parametrize("N", [2, 4, 7])
+def test_free_stream(N):
+    check_free_stream(oracle.default(), N)
+
+
+def check_isothermal_hydrostatic(orc, N, random_metrics):
+    """u = 0, rho = rho0 exp(-phi/(R T0)), p = rho R T0, any phi: the pair flux is
+    p_i e_j exactly, so rhs^rho = rhs^E = 0 bitwise and
+    rhs^m_i = -(p_i/J_i) sum_k [ (D^k Ja^k_m)(i) - 2 D[i_k][i_k] Ja^k_m(i) ]."""
+    rng = np.random.default_rng(80 + N)
+    D = I.diff_matrix(N)
+    X = I.box_mesh((2, 1, 2), (0, 0, 0), (2000, 1000, 2000), N, warp_frac=0.05, seed=N,
+                   warp_wavelength=(1000, 1000, 1000))
+    geom = I.metrics(X, D)
+    if random_metrics:
+        geom[:9] = rng.uniform(-1e6, 1e6, geom[:9].shape)
+    ne = X.shape[1]
+    Xf = X.reshape(3, ne, -1)
+    T0 = 280.0
+    phi = I.GRAV * Xf[2] + 50.0 * np.sin(Xf[0] / 300.0)  # any geopotential field
+    rho = 1.1 * np.exp(-phi / (I.R_GAS * T0))
+    p = rho * I.R_GAS * T0
+    q = I.conserved(rho, np.zeros((3,) + rho.shape), p, phi)
+    rhs = orc.volume_rhs(q, phi, geom, D, N)
+    assert np.all(rhs[0] == 0.0) and np.all(rhs[4] == 0.0)
+    for e in range(ne):
+        dt, dg = dterm(D, geom[:, e], N), diag_term(D, geom[:, e], N)
+        for m in range(3):
+            expect = -p[e] * (dt[m] - 2 * dg[m]) / geom[9, e]
+            scale = (p[e] * (np.abs(geom[3 * np.arange(3)[:, None] + m, e]).sum(0))
+                     * np.abs(D).sum(1).max() * 2 / geom[9, e]).max()
+            assert np.abs(rhs[1 + m, e] - expect).max() <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("N,random_metrics", [(3, False), (4, True), (7, False)])
+def test_isothermal_hydrostatic(N, random_metrics):
+    check_isothermal_hydrostatic(oracle.default(), N, random_metrics)
+
+
+def check_cartesian_reduction(orc, N):
+    """Affine axis-aligned elements: rhs_i = -sum_k (4/h_k) sum_{l != i_k} D[i_k][l] F_k(q_i, q_l),
+    assembled here along lines with the oracle's pair flux."""
+    rng = np.random.default_rng(90 + N)
+    D = I.diff_matrix(N)
+    h = np.array([0.5, 2.0, 1.25])
+    X = I.box_mesh((2, 1, 1), (0, 0, 0), (2 * h[0], h[1], h[2]), N)
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    Nq = N + 1
+    rho, u, p, phi = random_prims(rng, ne * Nq ** 3)
+    q = cons(rho, u, p, phi).T.reshape(5, ne, -1).copy()
+    phi = phi.reshape(ne, -1)
+    rhs = orc.volume_rhs(q, phi, geom, D, N)
+    qe = q.reshape(5, ne, Nq, Nq, Nq)   # [f][e][c][b][a]
+    pe = phi.reshape(ne, Nq, Nq, Nq)
+    expect = np.zeros((5, ne, Nq, Nq, Nq))
+    for e in range(ne):
+        for c in range(Nq):
+            for b in range(Nq):
+                for a in range(Nq):
+                    idx = (c, b, a)
+                    for k in range(3):
+                        ax = 2 - k  # position of xi_k in (c, b, a)
+                        for l in range(Nq):
+                            if l == idx[ax]:
+                                continue
+                            jdx = list(idx); jdx[ax] = l; jdx = tuple(jdx)
+                            F = orc.ec_flux(qe[(slice(None), e) + idx], pe[(e,) + idx],
+                                               qe[(slice(None), e) + jdx], pe[(e,) + jdx], k)[0]
+                            expect[(slice(None), e) + idx] -= (4 / h[k]) * D[idx[ax], l] * F
+    expect = expect.reshape(5, ne, -1)
+    for f in range(5):
+        assert np.abs(rhs[f] - expect[f]).max() <= 1e-13 * np.abs(expect[f]).max()
+
+
+@pytest.mark.parametrize("N", [1, 3, 4])
+def test_cartesian_reduction(N):
+    check_cartesian_reduction(oracle.default(), N)
