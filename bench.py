@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the ESDG flux-differencing volume term on one MI355X.
+
+A step is one evaluation of the whole volume term (one kernel launch of
+libesdg) over one batch of synthetic input: the rising-bubble-shaped workload
+(16^3 affine hexes, N=4, 512,000 DOF) in fp64.  Inputs are resident in HBM
+before the timed region; consecutive steps rotate over enough distinct buffer
+sets (> 512 MB in total) that no step finds its inputs in the 256 MB
+Infinity Cache left behind by the previous one.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "bubble"
+METRIC = "volume-RHS DOF-updates/s and FP64 GFLOP/s (% of FP64 vector peak), N=4, 1 GPU"
+SOURCES = ("entropy_stable_dg_amd/csrc/volume_kernel.hpp", "entropy_stable_dg_amd/csrc/esdg_api.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, dtype: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(f"{workload}_{dtype}")
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
+    """Returns (seconds per step rotating cold buffers, seconds per step hot, info)."""
+    import torch
+
+    from entropy_stable_dg_amd import esdg, inputs, perfmodel
+
+    wl = inputs.make(name)
+    dtype = "f32" if wl.q.dtype.name == "float32" else "f64"
+    dev = torch.device("cuda:0")
+    footprint = sum(a.nbytes for a in (wl.q, wl.phi, wl.geom)) + wl.q.nbytes
+    nsets = max(2, math.ceil(rotate_bytes / footprint))
+    log(f"{name}: N={wl.N} nelem={wl.nelem} dof={wl.dof} dtype={dtype} "
+        f"footprint={footprint / 1e6:.1f} MB x {nsets} buffer sets")
+    host = [torch.from_numpy(a) for a in (wl.q, wl.phi, wl.geom, wl.D)]
+    sets = []
+    for _ in range(nsets):
+        q, phi, geom, D = (t.to(dev) for t in host)
+        rhs = torch.empty_like(q)
+        sets.append((q, phi, geom, D, rhs))
+    fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    ptrs = [(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), rhs.data_ptr())
+            for q, phi, geom, D, rhs in sets]
+    N, nelem = wl.N, wl.nelem
+
+    def run(k: int, rotate: bool) -> None:
+        for i in range(k):
+            p = ptrs[i % nsets] if rotate else ptrs[0]
+            st = fn(p[0], p[1], p[2], p[3], N, nelem, p[4], handle)
+            if st != 0:
+                raise RuntimeError(esdg.esdg_status_string(st))
+
+    results = {}
+    for rotate in (True, False):
+        run(warmup, rotate)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        run(steps, rotate)
+        end.record(stream)
+        torch.cuda.synchronize()
+        results[rotate] = start.elapsed_time(end) * 1e-3 / steps
+        log(f"{name}: {'rotating' if rotate else 'hot'} {results[rotate] * 1e6:.2f} us/step")
+    info = dict(N=N, nelem=nelem, dof=wl.dof, dtype=dtype, description=wl.description,
+                seed=wl.seed, buffer_sets=nsets,
+                bytes=perfmodel.algorithmic_bytes(N, nelem, dtype),
+                flops=perfmodel.flops_per_element(N) * nelem)
+    del sets
+    torch.cuda.empty_cache()
+    return results[True], results[False], info, wl
+
+
+def cpu_baseline(wl, min_seconds: float):
+    import oracle
+
+    threads = oracle.max_threads()
+    oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)  # warm (library load, pages)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    value = wl.dof * reps / dt
+    log(f"cpu oracle: {reps} full evaluations in {dt:.1f} s on {threads} threads -> {value:.3e} DOF/s")
+    return {"value": value, "unit": "DOF-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} evaluations of the whole {wl.name} workload ({wl.dof} DOF each), "
+                      f"{dt:.1f} s, fp64 ordered pairs, OpenMP over elements"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--rotate-mb", type=float, default=512.0,
+                    help="total size of the rotating buffer sets (MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extra", default="bubble_f32",
+                    help="comma-separated extra workloads to time (reported under 'extra')")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the volume term is element-local: each GPU would run the same kernel on its "
+              "own elements with no communication)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from entropy_stable_dg_amd import esdg, perfmodel
+
+    if not os.path.exists(esdg.LIB_PATH):
+        from entropy_stable_dg_amd import build as hip_build
+        hip_build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"device: {torch.cuda.get_device_name(0)}; kernel source {kernel_source_hash()}")
+
+    t_cold, t_hot, info, wl = time_workload(HEADLINE, args.steps, args.warmup, args.rotate_mb * 1e6)
+    value = info["dof"] / t_cold
+    achieved_gbs = info["bytes"] / t_cold / 1e9
+    gflops = info["flops"] / t_cold / 1e9
+    traffic = measured_traffic(HEADLINE, info["dtype"])
+
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x]:
+        c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6)
+        extra[name] = {
+            "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
+            "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
+            "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
+        }
+        if inf["dtype"] == "f32" and inf["N"] == info["N"] and inf["nelem"] == info["nelem"]:
+            extra[name]["speedup_over_fp64"] = (inf["dof"] / c) / value
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "DOF-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_cold * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": info["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": "rising-bubble-shaped 16x16x16 affine hexes on [0,1000]^3 m, N=4, "
+                        "512000 DOF, fp64",
+            "N": info["N"], "nelem": info["nelem"], "dof": info["dof"], "seed": info["seed"],
+            "buffer_sets": info["buffer_sets"], "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": perfmodel.PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / perfmodel.PEAK_HBM_GBS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "gflops_analytic_fp64": gflops,
+        "frac_fp64_vector_peak": gflops / (perfmodel.PEAK_FP64_VECTOR_TFLOPS * 1e3),
+        "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
+        "hot_ms_per_step": t_hot * 1e3,
+        "hot_dof_per_s": info["dof"] / t_hot,
+        "kernel_source_hash": kernel_source_hash(),
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

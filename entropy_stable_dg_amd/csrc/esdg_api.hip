@@ -1,0 +1,111 @@
+// esdg_api.hip -- C ABI of libesdg: argument checks, launch configuration per
+// polynomial order, and the fp64 / fp32 entry points declared in esdg.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "esdg.h"
+#include "volume_kernel.hpp"
+
+namespace esdg {
+namespace {
+
+constexpr int kMinOrder = 1;
+constexpr int kMaxOrder = 8;
+
+// Launch shape per order: elements per workgroup and threads per workgroup,
+// chosen so that the 3 (N+1)^2 line tasks of EPB elements fill whole waves
+// as far as possible and the LDS footprint (15 values per node) leaves room
+// for two or more workgroups per CU.
+template <int N> struct Launch;
+template <> struct Launch<1> { static constexpr int EPB = 16, NT = 192; };  // 192/192 lines
+template <> struct Launch<2> { static constexpr int EPB = 7, NT = 192; };   // 189/192
+template <> struct Launch<3> { static constexpr int EPB = 4, NT = 192; };   // 192/192
+template <> struct Launch<4> { static constexpr int EPB = 4, NT = 320; };   // 300/320
+template <> struct Launch<5> { static constexpr int EPB = 1, NT = 128; };   // 108/128
+template <> struct Launch<6> { static constexpr int EPB = 1, NT = 192; };   // 147/192
+template <> struct Launch<7> { static constexpr int EPB = 1, NT = 192; };   // 192/192
+template <> struct Launch<8> { static constexpr int EPB = 1, NT = 256; };   // 243/256
+
+template <typename T, int N>
+int launch(const T *q, const T *phi, const T *geom, const T *D, int64_t nelem, T *rhs,
+           hipStream_t stream)
+{
+    constexpr int EPB = Launch<N>::EPB, NT = Launch<N>::NT;
+    const int64_t blocks = (nelem + EPB - 1) / EPB;
+    if (blocks > INT32_MAX) return ESDG_ERR_NELEM;
+    hipLaunchKernelGGL((volume_rhs_kernel<T, N, EPB, NT>), dim3((unsigned)blocks), dim3(NT), 0,
+                       stream, q, phi, geom, D, nelem, rhs);
+    return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+template <typename T>
+int volume_rhs(const T *q, const T *phi, const T *geom, const T *D, int N, int64_t nelem, T *rhs,
+               hipStream_t stream)
+{
+    if (N < kMinOrder || N > kMaxOrder) return ESDG_ERR_ORDER;
+    if (nelem < 0) return ESDG_ERR_NELEM;
+    if (nelem == 0) return ESDG_OK;
+    if (!q || !phi || !geom || !D || !rhs) return ESDG_ERR_NULL;
+    const int64_t Nq = N + 1, Np = Nq * Nq * Nq;
+    // the largest array has 10 * nelem * Np elements of T
+    if (nelem > INT64_MAX / (10 * Np * (int64_t)sizeof(T))) return ESDG_ERR_NELEM;
+    const int64_t field = nelem * Np * (int64_t)sizeof(T);
+    const int64_t rbytes = 5 * field;
+    if (overlaps(rhs, rbytes, q, 5 * field) || overlaps(rhs, rbytes, phi, field) ||
+        overlaps(rhs, rbytes, geom, 10 * field) ||
+        overlaps(rhs, rbytes, D, Nq * Nq * (int64_t)sizeof(T)))
+        return ESDG_ERR_ALIAS;
+    switch (N) {
+        case 1: return launch<T, 1>(q, phi, geom, D, nelem, rhs, stream);
+        case 2: return launch<T, 2>(q, phi, geom, D, nelem, rhs, stream);
+        case 3: return launch<T, 3>(q, phi, geom, D, nelem, rhs, stream);
+        case 4: return launch<T, 4>(q, phi, geom, D, nelem, rhs, stream);
+        case 5: return launch<T, 5>(q, phi, geom, D, nelem, rhs, stream);
+        case 6: return launch<T, 6>(q, phi, geom, D, nelem, rhs, stream);
+        case 7: return launch<T, 7>(q, phi, geom, D, nelem, rhs, stream);
+        case 8: return launch<T, 8>(q, phi, geom, D, nelem, rhs, stream);
+    }
+    return ESDG_ERR_ORDER;
+}
+
+}  // namespace
+}  // namespace esdg
+
+extern "C" {
+
+int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom, const double *D,
+                        int N, int64_t nelem, double *rhs, hipStream_t stream)
+{
+    return esdg::volume_rhs<double>(q, phi, geom, D, N, nelem, rhs, stream);
+}
+
+int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom, const float *D,
+                        int N, int64_t nelem, float *rhs, hipStream_t stream)
+{
+    return esdg::volume_rhs<float>(q, phi, geom, D, N, nelem, rhs, stream);
+}
+
+const char *esdg_status_string(int status)
+{
+    switch (status) {
+        case ESDG_OK: return "ok";
+        case ESDG_ERR_NULL: return "a required pointer is NULL";
+        case ESDG_ERR_ORDER: return "polynomial order N outside the compiled range";
+        case ESDG_ERR_NELEM: return "nelem is negative or too large";
+        case ESDG_ERR_LAUNCH: return "kernel launch failed";
+        case ESDG_ERR_ALIAS: return "rhs overlaps an input array";
+    }
+    return "unknown status";
+}
+
+int esdg_min_order(void) { return esdg::kMinOrder; }
+int esdg_max_order(void) { return esdg::kMaxOrder; }
+
+}  // extern "C"

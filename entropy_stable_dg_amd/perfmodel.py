@@ -1,0 +1,54 @@
+"""Work and traffic model of the volume term, and MI355X peak figures.
+
+Algorithmic traffic per node (DOF): the kernel must read 5 conserved fields,
+the geopotential and 10 geometry values (9 metric terms and J) and write 5
+fields: 21 values = 168 B in fp64, 84 B in fp32.  The differentiation matrix
+(N+1)^2 values per launch is added once.
+
+FLOP counting convention (counted from the kernel's arithmetic; the method's
+work, not the ordered-pair work the symmetric evaluation avoids):
+  +, -, x, / and reciprocal = 1 FLOP, fused multiply-add = 2, log = 1;
+  comparisons and selects = 0; the log means are counted on their series
+  branch; quantities hoisted per node are counted once per node.
+  per unordered pair on a line ........ 120
+  per node (primitives, p, b, 2 logs,
+            1/b, direction sum, -1/J) ...  38
+Unordered pairs per element: 3 (N+1)^2 (N+1) N / 2.
+"""
+from __future__ import annotations
+
+FLOP_PER_PAIR = 120
+FLOP_PER_NODE = 38
+
+# MI355X (gfx950) published peaks
+PEAK_HBM_GBS = 8000.0          # HBM3E, GB/s
+PEAK_FP64_VECTOR_TFLOPS = 78.6
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+CU_COUNT = 256
+CLOCK_GHZ = 2.4
+
+
+def pairs_per_element(N: int) -> int:
+    Nq = N + 1
+    return 3 * Nq * Nq * (Nq * (Nq - 1) // 2)
+
+
+def flops_per_element(N: int) -> int:
+    return pairs_per_element(N) * FLOP_PER_PAIR + (N + 1) ** 3 * FLOP_PER_NODE
+
+
+def flops_per_dof(N: int) -> float:
+    return flops_per_element(N) / (N + 1) ** 3
+
+
+def bytes_per_dof(dtype: str) -> int:
+    return 21 * (8 if dtype == "f64" else 4)
+
+
+def algorithmic_bytes(N: int, nelem: int, dtype: str) -> int:
+    size = 8 if dtype == "f64" else 4
+    return nelem * (N + 1) ** 3 * bytes_per_dof(dtype) + (N + 1) ** 2 * size
+
+
+def arithmetic_intensity(N: int, dtype: str) -> float:
+    return flops_per_dof(N) / bytes_per_dof(dtype)

@@ -1,0 +1,79 @@
+/*
+ * esdg.h -- C ABI of the ESDG flux-differencing volume-term library
+ * (libesdg.so, HIP for AMD gfx950).
+ *
+ * The operation is the volume term of the semi-discrete entropy-stable DG
+ * form of "GPU Performance of an Entropy-Stable Discontinuous Galerkin Euler
+ * Solver with Non-Conservative Terms" (arXiv 2605.16684v2): §3, Eq. 2 (the
+ * volume part, source h = 0), with the two-point entropy-conservative flux of
+ * §4.1, Eq. 3-5 and the non-conservative gravity term split as in §4.1.
+ * Per node i of element e, with i_k its index along reference direction k and
+ * l running over the other nodes of the k-line through i:
+ *
+ *   rhs_i = -(1/J_i) sum_{k=1..3} sum_{l != i_k} D[i_k][l]
+ *                    sum_{j=1..3} (Ja^k_j(i) + Ja^k_j(l)) F_j(q_i, q_l)
+ *
+ * where F_j(q_i, q_l) is the two-point flux in physical direction j with the
+ * receiving node i as the "-" state (Eq. 4-5) and gamma = 1.4.
+ *
+ * Layouts (all arrays contiguous, Nq = N+1, Np = Nq^3, node index
+ * n = a + Nq*(b + Nq*c) with a, b, c the indices along xi_1, xi_2, xi_3):
+ *   q     [5][nelem][Np]   rho, rho*u1, rho*u2, rho*u3, E (E includes rho*phi)
+ *   phi   [nelem][Np]      geopotential
+ *   geom  [10][nelem][Np]  Ja^1_1, Ja^1_2, Ja^1_3, Ja^2_1, ..., Ja^3_3, J,
+ *                          Ja^k_j = J * d(xi_k)/d(x_j), J > 0
+ *   D     [Nq][Nq]         row-major, D[a][l] = l_l'(xi_a) on the LGL nodes
+ *                          (must satisfy the SBP property of an LGL
+ *                          collocation operator; only D[a][l], l != a, is read)
+ *   rhs   [5][nelem][Np]   OUTPUT, overwritten
+ *
+ * Ownership and semantics:
+ *   - Every pointer is a DEVICE pointer to memory owned by the caller; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - rhs must not overlap any input (checked: ESDG_ERR_ALIAS).
+ *   - The call is asynchronous on `stream` (0 = the null stream) and never
+ *     synchronises; it is thread-safe and re-entrant.
+ *   - nelem == 0 returns ESDG_OK without launching (pointers are not read).
+ *   - Argument errors are returned synchronously, before any HIP call.
+ *   - Not checked (preconditions): rho > 0, p > 0, J > 0, finite values.
+ *     Violations give NaN/Inf in rhs; they never cause out-of-bounds access.
+ *   - Pointers must be aligned to the element type.
+ */
+#ifndef ESDG_H
+#define ESDG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ESDG_OK          0
+#define ESDG_ERR_NULL   (-1)  /* a required pointer is NULL (nelem > 0)             */
+#define ESDG_ERR_ORDER  (-2)  /* N outside [esdg_min_order(), esdg_max_order()]     */
+#define ESDG_ERR_NELEM  (-3)  /* nelem < 0, or the arrays would not be addressable  */
+#define ESDG_ERR_LAUNCH (-4)  /* the kernel launch failed (hipGetLastError)         */
+#define ESDG_ERR_ALIAS  (-5)  /* rhs overlaps an input array                        */
+
+/* Volume term in fp64 arithmetic. Returns a status code above. */
+int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom,
+                        const double *D, int N, int64_t nelem, double *rhs,
+                        hipStream_t stream);
+
+/* Volume term in fp32 arithmetic (fp32 inputs and output); same contract. */
+int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom,
+                        const float *D, int N, int64_t nelem, float *rhs,
+                        hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *esdg_status_string(int status);
+
+/* Range of polynomial orders N compiled into the library. */
+int esdg_min_order(void);
+int esdg_max_order(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ESDG_H */

@@ -1,0 +1,93 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/esdg.h declares, and rejects bad arguments synchronously, before any
+HIP call (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from entropy_stable_dg_amd import esdg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "esdg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(esdg_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(esdg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = esdg.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen(f"nm -D --defined-only {esdg.LIB_PATH}").read()
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_order_range_and_status_strings():
+    assert esdg.esdg_min_order() == 1
+    assert esdg.esdg_max_order() == 8
+    for st in (esdg.ESDG_OK, esdg.ESDG_ERR_NULL, esdg.ESDG_ERR_ORDER, esdg.ESDG_ERR_NELEM,
+               esdg.ESDG_ERR_LAUNCH, esdg.ESDG_ERR_ALIAS):
+        s = esdg.esdg_status_string(st)
+        assert s and s != "unknown status"
+    assert esdg.esdg_status_string(12345) == "unknown status"
+
+
+# Fake, never-dereferenced addresses: every call below fails validation (or is
+# the nelem == 0 no-op) before the library touches the HIP runtime.
+A, B, C, Dp, R = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+@pytest.mark.parametrize("fn", [esdg.esdg_volume_rhs_f64, esdg.esdg_volume_rhs_f32])
+def test_argument_errors(fn):
+    assert fn(A, B, C, Dp, 0, 1, R, 0) == esdg.ESDG_ERR_ORDER
+    assert fn(A, B, C, Dp, 9, 1, R, 0) == esdg.ESDG_ERR_ORDER
+    assert fn(A, B, C, Dp, -1, 1, R, 0) == esdg.ESDG_ERR_ORDER
+    assert fn(A, B, C, Dp, 4, -1, R, 0) == esdg.ESDG_ERR_NELEM
+    assert fn(A, B, C, Dp, 4, 2 ** 62, R, 0) == esdg.ESDG_ERR_NELEM
+    # nelem == 0: OK without reading any pointer
+    assert fn(0, 0, 0, 0, 4, 0, 0, 0) == esdg.ESDG_OK
+    for i in range(5):
+        args = [A, B, C, Dp, R]
+        args[i] = 0
+        assert fn(args[0], args[1], args[2], args[3], 4, 10, args[4], 0) == esdg.ESDG_ERR_NULL
+    # the order check comes first, then nelem, then pointers
+    assert fn(0, 0, 0, 0, 0, -1, 0, 0) == esdg.ESDG_ERR_ORDER
+    assert fn(0, 0, 0, 0, 3, -1, 0, 0) == esdg.ESDG_ERR_NELEM
+
+
+@pytest.mark.parametrize("fn,size", [(esdg.esdg_volume_rhs_f64, 8), (esdg.esdg_volume_rhs_f32, 4)])
+def test_alias_errors(fn, size):
+    N, nelem = 3, 100
+    field = nelem * 64 * size
+    # rhs overlapping the last field of q, phi, the geometry, or D
+    assert fn(A, B, C, Dp, N, nelem, A + 4 * field, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, N, nelem, B - 5 * field + size, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, N, nelem, C + 9 * field, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, N, nelem, Dp + 8, 0) == esdg.ESDG_ERR_ALIAS
+
+
+def test_tensor_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(5, 1, 8, dtype=torch.float64)
+    phi = torch.zeros(1, 8, dtype=torch.float64)
+    geom = torch.zeros(10, 1, 8, dtype=torch.float64)
+    D = torch.zeros(2, 2, dtype=torch.float64)
+    with pytest.raises(ValueError, match="GPU"):
+        esdg.volume_rhs(q, phi, geom, D)
+    with pytest.raises(TypeError):
+        esdg.volume_rhs(q.float(), phi, geom, D)

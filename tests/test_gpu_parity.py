@@ -1,0 +1,247 @@
+"""GPU parity of libesdg against the CPU oracle (element by element), plus the
+oracle's identities re-checked on GPU output.
+
+Tolerance: per field, max_i |rhs_gpu - rhs_oracle| / max_i |rhs_oracle|
+  <= 1e-11 in fp64, <= 2e-5 in fp32 (against the fp64 oracle, both on the
+  fp32-rounded inputs promoted exactly and on the original fp64 inputs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import esdg
+from entropy_stable_dg_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float64: 1e-11, np.float32: 2e-5}
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_gpu(*arrays):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(dev()) for a in arrays]
+
+
+def gpu_rhs(q, phi, geom, D):
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    out = esdg.volume_rhs(tq, tp, tg, tD)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def field_errors(got, ref):
+    got = got.astype(np.float64)
+    return [float(np.abs(got[f] - ref[f]).max() / np.abs(ref[f]).max()) for f in range(5)]
+
+
+def check(got, ref, tol, label):
+    err = field_errors(got, ref)
+    print(f"[parity] {label}: max rel err per field {['%.2e' % e for e in err]}", flush=True)
+    assert max(err) <= tol, (label, err)
+
+
+@pytest.fixture(scope="module")
+def workloads():
+    return {}
+
+
+def get(workloads, name):
+    if name not in workloads:
+        workloads[name] = I.make(name)
+    return workloads[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "bubble", "baroclinic", "high_order"])
+def test_fp64_workloads(workloads, name):
+    wl = get(workloads, name)
+    print(f"[parity] {name}: N={wl.N} nelem={wl.nelem} dof={wl.dof}", flush=True)
+    got = gpu_rhs(wl.q, wl.phi, wl.geom, wl.D)
+    ref = oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)
+    check(got, ref, TOL[np.float64], name)
+
+
+def test_fp32_bubble(workloads):
+    wl32 = get(workloads, "bubble_f32")
+    wl64 = get(workloads, "bubble")
+    got = gpu_rhs(wl32.q, wl32.phi, wl32.geom, wl32.D)
+    assert got.dtype == np.float32
+    ref_rounded = oracle.volume_rhs(wl32.q, wl32.phi, wl32.geom, wl32.D, wl32.N)
+    check(got, ref_rounded, TOL[np.float32], "bubble fp32 vs oracle(fp32-rounded inputs)")
+    ref64 = oracle.volume_rhs(wl64.q, wl64.phi, wl64.geom, wl64.D, wl64.N)
+    check(got, ref64, TOL[np.float32], "bubble fp32 vs oracle(fp64 inputs)")
+
+
+@pytest.mark.parametrize("name", ["tiny", "baroclinic"])
+def test_fp32_other_workloads(workloads, name):
+    wl = get(workloads, name)
+    q, phi, geom, D = (a.astype(np.float32) for a in (wl.q, wl.phi, wl.geom, wl.D))
+    got = gpu_rhs(q, phi, geom, D)
+    ref = oracle.volume_rhs(q, phi, geom, D, wl.N)
+    check(got, ref, TOL[np.float32], f"{name} fp32")
+
+
+def random_workload(N, nelem_xyz=(3, 2, 1), seed=0):
+    """Warped mesh, smooth but strongly varying state (rho, p vary by tens of
+    percent, |u| up to ~50 m/s), so every code path (series and log branches
+    of the log means) is exercised."""
+    rng = np.random.default_rng(seed)
+    K = nelem_xyz
+    hi = (1000.0 * K[0], 1000.0 * K[1], 1000.0 * K[2])
+    D = I.diff_matrix(N)
+    X = I.box_mesh(K, (0, 0, 0), hi, N, warp_frac=0.05, seed=seed, warp_wavelength=(1000, 1000, 1000))
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    x, y, z = X.reshape(3, ne, -1)
+    k = rng.uniform(1.0, 3.0, 6) / 1000.0
+    rho = 1.0 + 0.3 * np.sin(k[0] * x + k[1] * y) * np.cos(k[2] * z)
+    u = np.stack([30 * np.sin(k[3] * y + 1e-3 * z), 20 * np.cos(k[4] * x - 1e-3 * y),
+                  10 * np.sin(k[5] * z + 1e-3 * x)])
+    u += rng.uniform(-1, 1, u.shape)
+    p = 1e5 * (1 + 0.2 * np.cos(k[1] * x + k[2] * z)) * (1 + 1e-3 * rng.uniform(-1, 1, x.shape))
+    phi = I.GRAV * z
+    q = I.conserved(rho, u, p, phi)
+    return q, phi, geom, D
+
+
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_every_order_random_state(N, dtype):
+    q, phi, geom, D = random_workload(N, seed=N)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_rhs(q, phi, geom, D)
+    ref = oracle.volume_rhs(q, phi, geom, D, N)
+    check(got, ref, TOL[dtype], f"random N={N} {np.dtype(dtype).name}")
+
+
+@pytest.mark.parametrize("nelem", [1, 3, 5, 7, 4093])
+def test_ragged_element_counts(workloads, nelem):
+    """Element counts that leave the last workgroup partly empty."""
+    wl = get(workloads, "bubble")
+    sel = slice(4096 - nelem, 4096)
+    q, phi, geom = wl.q[:, sel], wl.phi[sel], wl.geom[:, sel]
+    got = gpu_rhs(q, phi, geom, wl.D)
+    ref = oracle.volume_rhs(q, phi, geom, wl.D, wl.N)
+    check(got, ref, TOL[np.float64], f"bubble tail nelem={nelem}")
+
+
+def test_nelem_zero_is_a_noop():
+    N = 4
+    Np = (N + 1) ** 3
+    q = torch.zeros(5, 0, Np, dtype=torch.float64, device=dev())
+    phi = torch.zeros(0, Np, dtype=torch.float64, device=dev())
+    geom = torch.zeros(10, 0, Np, dtype=torch.float64, device=dev())
+    D = torch.zeros(N + 1, N + 1, dtype=torch.float64, device=dev())
+    out = esdg.volume_rhs(q, phi, geom, D)
+    torch.cuda.synchronize()
+    assert out.shape == (5, 0, Np)
+
+
+def test_bitwise_repeatable(workloads):
+    wl = get(workloads, "baroclinic")
+    a = gpu_rhs(wl.q, wl.phi, wl.geom, wl.D)
+    b = gpu_rhs(wl.q, wl.phi, wl.geom, wl.D)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_non_default_stream(workloads):
+    wl = get(workloads, "tiny")
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    s = torch.cuda.Stream()
+    ref = esdg.volume_rhs(tq, tp, tg, tD)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = esdg.volume_rhs(tq, tp, tg, tD, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+def test_full_size_mesh_by_element_locality(workloads):
+    """The pages' N=4, L=6 bubble mesh size (262,144 elements, 32,768,000 DOF):
+    the bubble workload tiled 64 times must give the small run's result, tiled,
+    bitwise (the volume term is element-local and the kernel deterministic);
+    a sample of elements is also checked against the oracle."""
+    wl = get(workloads, "bubble")
+    reps = 64
+    small = gpu_rhs(wl.q, wl.phi, wl.geom, wl.D)
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    big_q, big_p, big_g = tq.repeat(1, reps, 1), tp.repeat(reps, 1), tg.repeat(1, reps, 1)
+    assert big_q.shape[1] == 262144 and big_q.shape[1] * big_q.shape[2] == 32768000
+    out = esdg.volume_rhs(big_q, big_p, big_g, tD)
+    torch.cuda.synchronize()
+    big = out.cpu().numpy()
+    assert np.array_equal(big.reshape(5, reps, wl.nelem, -1)[:, 17], small)
+    assert np.array_equal(big.reshape(5, reps, wl.nelem, -1)[:, -1], small)
+    rng = np.random.default_rng(0)
+    idx = rng.choice(262144, 64, replace=False)
+    ref = oracle.volume_rhs(wl.q[:, idx % wl.nelem], wl.phi[idx % wl.nelem],
+                            wl.geom[:, idx % wl.nelem], wl.D, wl.N)
+    check(big[:, idx], ref, TOL[np.float64], "L=6 mesh, sampled elements")
+
+
+# --- identities on GPU output -------------------------------------------------
+def test_isothermal_hydrostatic_on_gpu():
+    N = 4
+    D = I.diff_matrix(N)
+    X = I.box_mesh((4, 2, 3), (0, 0, 0), (4000, 2000, 3000), N, warp_frac=0.05, seed=1,
+                   warp_wavelength=(1000, 1000, 1000))
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    z = X.reshape(3, ne, -1)[2]
+    phi = I.GRAV * z
+    T0 = 280.0
+    rho = 1.1 * np.exp(-phi / (I.R_GAS * T0))
+    p = rho * I.R_GAS * T0
+    q = I.conserved(rho, np.zeros((3,) + rho.shape), p, phi)
+    got = gpu_rhs(q, phi, geom, D)
+    assert np.all(got[0] == 0.0) and np.all(got[4] == 0.0)
+    ref = oracle.volume_rhs(q, phi, geom, D, N)
+    for f in (1, 2, 3):
+        assert np.abs(got[f] - ref[f]).max() <= 1e-11 * np.abs(ref[f]).max()
+    # interior nodes balance to round-off relative to the face values
+    idx = np.arange(N + 1)
+    inner = (idx > 0) & (idx < N)
+    interior = np.einsum("c,b,a->cba", inner, inner, inner).ravel()
+    scale = np.abs(got[1:4]).max()
+    assert np.abs(got[1:4][:, :, interior]).max() <= 1e-10 * scale
+
+
+def test_entropy_identity_on_gpu():
+    """sum_i w_i J_i v_i . rhs_i equals the boundary entropy-flux term minus the
+    metric-residual term, evaluated on the GPU result."""
+    N = 4
+    q, phi, geom, D = random_workload(N, nelem_xyz=(2, 2, 1), seed=11)
+    got = gpu_rhs(q, phi, geom, D)
+    _, w = I.lgl(N)
+    Nq = N + 1
+    W = np.einsum("c,b,a->cba", w, w, w).ravel()
+    rho = q[0]
+    u = q[1:4] / rho
+    p = (I.GAMMA - 1) * (q[4] - 0.5 * rho * (u ** 2).sum(0) - rho * phi)
+    s = np.log(p) - I.GAMMA * np.log(rho)
+    b = rho / (2 * p)
+    v = np.stack([(I.GAMMA - s) / (I.GAMMA - 1) - b * (u ** 2).sum(0) + 2 * b * phi,
+                  2 * b * u[0], 2 * b * u[1], 2 * b * u[2], -2 * b])
+    for e in range(q.shape[1]):
+        terms = W * geom[9, e] * (v[:, e] * got[:, e])
+        lhs = terms.sum()
+        g = geom[:, e].reshape(10, Nq, Nq, Nq)
+        psi = (rho[e] * u[:, e]).reshape(3, Nq, Nq, Nq)
+        bnd = 0.0
+        for k in range(3):
+            contra = sum(g[3 * k + j] * psi[j] for j in range(3))
+            if k == 0:
+                bnd += np.einsum("c,b,cb->", w, w, contra[:, :, -1] - contra[:, :, 0])
+            elif k == 1:
+                bnd += np.einsum("c,a,ca->", w, w, contra[:, -1, :] - contra[:, 0, :])
+            else:
+                bnd += np.einsum("b,a,ba->", w, w, contra[-1, :, :] - contra[0, :, :])
+        resid = 0.0
+        for j in range(3):
+            dj = (I._apply_d(D, g[j], 0) + I._apply_d(D, g[3 + j], 1) + I._apply_d(D, g[6 + j], 2))
+            resid += (W * (psi[j] * dj).ravel()).sum()
+        assert abs(lhs - (bnd - resid)) <= 1e-12 * np.abs(terms).sum()

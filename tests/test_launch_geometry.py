@@ -1,0 +1,88 @@
+"""Host-side check of the volume kernel's launch geometry: the index arithmetic
+of every phase, replayed on the CPU for every compiled order, stays inside the
+buffers it touches, and each (direction, node) partial-sum slot in LDS is
+written by exactly one line thread.  Mirrors entropy_stable_dg_amd/csrc
+(volume_kernel.hpp and the launch table in esdg_api.hip)."""
+import re
+
+import numpy as np
+import pytest
+
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+API = os.path.join(ROOT, "entropy_stable_dg_amd", "csrc", "esdg_api.hip")
+KERNEL = os.path.join(ROOT, "entropy_stable_dg_amd", "csrc", "volume_kernel.hpp")
+
+NODE_VALUES = 19     # staged values per node (10 state values + 9 metric terms)
+PARTIAL_VALUES = 15  # 3 directions x 5 fields
+
+
+def launch_table():
+    text = open(API).read()
+    rows = re.findall(r"struct Launch<(\d+)>\s*\{\s*static constexpr int EPB = (\d+), NT = (\d+);", text)
+    return {int(n): (int(e), int(t)) for n, e, t in rows}
+
+
+def test_launch_table_covers_orders():
+    assert sorted(launch_table()) == list(range(1, 9))
+
+
+def test_staged_value_count_matches_kernel():
+    text = open(KERNEL).read()
+    m = re.search(r"enum NodeValue \{(.*?)\};", text, flags=re.S)
+    body = m.group(1)
+    assert "kJa + 9" in body
+    names = [x.strip().split("=")[0].strip() for x in body.split(",")]
+    assert names.index("kJa") + 9 == NODE_VALUES
+
+
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("nelem", [1, 2, 5, 13])
+def test_indices_in_bounds(N, nelem):
+    EPB, NT = launch_table()[N]
+    Nq = N + 1
+    Nq2, Np = Nq * Nq, Nq ** 3
+    NODES = EPB * Np
+    lds_values = max(NODE_VALUES, PARTIAL_VALUES) * NODES
+    lines = 3 * EPB * Nq2
+    assert lines <= NT
+    blocks = (nelem + EPB - 1) // EPB
+    fstride = nelem * Np
+    written = np.zeros((3, nelem * Np), dtype=int)
+    out_written = np.zeros(nelem * Np, dtype=int)
+    for blk in range(blocks):
+        e0 = blk * EPB
+        nvalid = min(EPB, nelem - e0) * Np
+        g0 = e0 * Np
+        # phase A / D: node threads
+        for t in range(NT):
+            for tt in range(t, nvalid, NT):
+                g = g0 + tt
+                assert 0 <= g and 4 * fstride + g < 5 * fstride and 9 * fstride + g < 10 * fstride
+                assert (NODE_VALUES - 1) * NODES + tt < lds_values
+                assert (10 + 4) * NODES + tt < lds_values
+                out_written[g] += 1
+        # phase B / C: line threads
+        for task in range(NT):
+            eb = task // (3 * Nq2)
+            r3 = task - eb * 3 * Nq2
+            k = r3 // Nq2
+            line = r3 - k * Nq2
+            p1, p2 = line % Nq, line // Nq
+            base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
+            step = [1, Nq, Nq2][k]
+            active = task < lines and eb * Np < nvalid
+            if not active:
+                continue
+            nb = eb * Np + base
+            for a in range(Nq):
+                s = nb + a * step
+                assert eb * Np <= s < (eb + 1) * Np <= NODES
+                assert (10 + 3 * k + 2) * NODES + s < lds_values   # staged reads
+                assert (k * 5 + 4) * NODES + s < lds_values         # partial writes
+                written[k, g0 + s] += 1
+                for l in range(a + 1, Nq):
+                    assert a * Nq + l < Nq2 and l * Nq + a < Nq2    # D reads
+    assert np.all(written == 1)
+    assert np.all(out_written == 1)
