@@ -109,6 +109,24 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
     return results[True], results[False], info, wl
 
 
+def profile_pass(steps: int) -> dict:
+    """Short run for hardware-counter collection under rocprofv3: one plain
+    copy kernel of known size (512 MiB read, 512 MiB written: the calibration
+    of FETCH_SIZE / WRITE_SIZE), then `steps` launches of the headline kernel."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = (512 << 20) // 8
+    src = torch.ones(n, dtype=torch.float64, device=dev)
+    dst = torch.empty_like(src)
+    torch.add(src, 0.0, out=dst)  # elementwise copy kernel: reads n*8 B, writes n*8 B
+    torch.cuda.synchronize()
+    del src, dst
+    cold, hot, info, _ = time_workload(HEADLINE, steps, 2, 512e6)
+    return {"profile_pass": True, "copy_bytes_each_way": n * 8, "us_per_step": cold * 1e6,
+            "bytes_per_launch": info["bytes"], "kernel_source_hash": kernel_source_hash()}
+
+
 def cpu_baseline(wl, min_seconds: float):
     import oracle
 
@@ -137,6 +155,8 @@ def main() -> int:
                     help="total size of the rotating buffer sets (MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3 counter passes (copy calibration + kernel)")
     ap.add_argument("--extra", default="bubble_f32",
                     help="comma-separated extra workloads to time (reported under 'extra')")
     args = ap.parse_args()
@@ -156,6 +176,9 @@ def main() -> int:
         hip_build.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}; kernel source {kernel_source_hash()}")
+    if args.profile_pass:
+        print(json.dumps(profile_pass(args.steps)), flush=True)
+        return 0
 
     t_cold, t_hot, info, wl = time_workload(HEADLINE, args.steps, args.warmup, args.rotate_mb * 1e6)
     value = info["dof"] / t_cold

@@ -13,28 +13,38 @@ namespace {
 constexpr int kMinOrder = 1;
 constexpr int kMaxOrder = 8;
 
-// Launch shape per order: elements per workgroup and threads per workgroup,
-// chosen so that the 3 (N+1)^2 line tasks of EPB elements fill whole waves
-// as far as possible and the LDS footprint (15 values per node) leaves room
-// for two or more workgroups per CU.
-template <int N> struct Launch;
-template <> struct Launch<1> { static constexpr int EPB = 16, NT = 192; };  // 192/192 lines
-template <> struct Launch<2> { static constexpr int EPB = 7, NT = 192; };   // 189/192
-template <> struct Launch<3> { static constexpr int EPB = 4, NT = 192; };   // 192/192
-template <> struct Launch<4> { static constexpr int EPB = 4, NT = 320; };   // 300/320
-template <> struct Launch<5> { static constexpr int EPB = 1, NT = 128; };   // 108/128
-template <> struct Launch<6> { static constexpr int EPB = 1, NT = 192; };   // 147/192
-template <> struct Launch<7> { static constexpr int EPB = 1, NT = 192; };   // 192/192
-template <> struct Launch<8> { static constexpr int EPB = 1, NT = 256; };   // 243/256
+// Launch shape per precision and order: EPB elements x NT threads per
+// workgroup (the 3 (N+1)^2 line tasks of EPB elements fill whole waves as far
+// as possible), and whether the metric terms are staged in LDS.  Chosen by
+// timing on MI355X at the bubble, baroclinic and N=4 L=6 mesh sizes.
+template <typename T, int N> struct Launch;
+// LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
+// registers, direction-major line order>
+template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
+template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
+template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false>; };              // 192/192
+template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, true, true>; };  // 225/256
+template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128>; };                        // 108/128
+template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192>; };                        // 147/192
+template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true>; }; // 192/192
+template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256>; };                        // 243/256
+template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
+template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
+template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192>; };
+template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true>; };
+template <> struct Launch<float, 5> { using C = LaunchCfg<1, 128, 0, false>; };
+template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false>; };
+template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false>; };
+template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false>; };
 
 template <typename T, int N>
 int launch(const T *q, const T *phi, const T *geom, const T *D, int64_t nelem, T *rhs,
            hipStream_t stream)
 {
-    constexpr int EPB = Launch<N>::EPB, NT = Launch<N>::NT;
-    const int64_t blocks = (nelem + EPB - 1) / EPB;
+    using C = typename Launch<T, N>::C;
+    const int64_t blocks = (nelem + C::EPB - 1) / C::EPB;
     if (blocks > INT32_MAX) return ESDG_ERR_NELEM;
-    hipLaunchKernelGGL((volume_rhs_kernel<T, N, EPB, NT>), dim3((unsigned)blocks), dim3(NT), 0,
+    hipLaunchKernelGGL((volume_rhs_kernel<T, N, C>), dim3((unsigned)blocks), dim3(C::NT), 0,
                        stream, q, phi, geom, D, nelem, rhs);
     return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
 }

@@ -50,13 +50,52 @@ constexpr double kBScale = 131072.0;
 
 template <typename T> struct Arith;
 
+// Natural log for positive normal doubles, for the per-node logs that feed the
+// log means.  x = m 2^e with m in [1/sqrt2, sqrt2); ln m = 2 atanh(s),
+// s = (m-1)/(m+1), |s| <= 0.1716, from the odd series of atanh truncated after
+// s^23 (remainder below 2e-19 relative); e ln2 is added in two parts (ln2 split
+// into a 32-bit head and a tail) so e ln2_hi is exact.  Absolute error is a
+// few ulp of |ln x|; only differences of two such logs larger than ~0.02 are
+// used, so this is ample.
+__device__ inline double ln_pos(double x)
+{
+    int e;
+    double m = frexp(x, &e);            // x = m 2^e, m in [0.5, 1)
+    if (m < 0.70710678118654752440) {   // move m into [1/sqrt2, sqrt2)
+        m = m + m;
+        e -= 1;
+    }
+    const double num = m - 1.0, den = m + 1.0;
+    double r = __builtin_amdgcn_rcp(den);
+    r = fma(r, fma(-den, r, 1.0), r);
+    r = fma(r, fma(-den, r, 1.0), r);
+    const double t = num * r;
+    const double t2 = t * t;
+    double p = 1.0 / 23.0;
+    p = fma(p, t2, 1.0 / 21.0);
+    p = fma(p, t2, 1.0 / 19.0);
+    p = fma(p, t2, 1.0 / 17.0);
+    p = fma(p, t2, 1.0 / 15.0);
+    p = fma(p, t2, 1.0 / 13.0);
+    p = fma(p, t2, 1.0 / 11.0);
+    p = fma(p, t2, 1.0 / 9.0);
+    p = fma(p, t2, 1.0 / 7.0);
+    p = fma(p, t2, 1.0 / 5.0);
+    p = fma(p, t2, 1.0 / 3.0);
+    const double lnm = fma(2.0 * t * t2, p, 2.0 * t);   // 2t + 2t^3 p(t^2)
+    const double ln2_hi = 0.693147180369123816490;       // 32 significant bits
+    const double ln2_lo = 1.90821492927058770002e-10;    // ln2 - ln2_hi
+    const double de = (double)e;
+    return fma(de, ln2_hi, fma(de, ln2_lo, lnm));
+}
+
 template <> struct Arith<double> {
     // series branch of the log mean when f = ((c-a)/(c+a))^2 < kSeries:
     // truncation after f^3 leaves an error below f^4/9 < 2e-17.
     static constexpr double kSeries = 1.0e-4;
     // node logs are natural logs
     static constexpr double kLogToLn = 1.0;
-    __device__ static inline double node_log(double x) { return log(x); }
+    __device__ static inline double node_log(double x) { return ln_pos(x); }
     // 1/x: hardware estimate refined by two Newton steps (error ~1 ulp)
     __device__ static inline double rcp(double x) {
         double r = __builtin_amdgcn_rcp(x);
@@ -76,6 +115,22 @@ template <> struct Arith<float> {
     __device__ static inline float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 };
 
+// Branch-free select of a and b on c.  Both operands are always computed
+// (they are a few multiplies each); a plain ?: lets the compiler sink their
+// computation into divergent branches, which costs more than it saves.
+__device__ inline double select(bool c, double a, double b)
+{
+    const unsigned long long ua = __builtin_bit_cast(unsigned long long, a);
+    const unsigned long long ub = __builtin_bit_cast(unsigned long long, b);
+    return __builtin_bit_cast(double, c ? ua : ub);
+}
+__device__ inline float select(bool c, float a, float b)
+{
+    const unsigned ua = __builtin_bit_cast(unsigned, a);
+    const unsigned ub = __builtin_bit_cast(unsigned, b);
+    return __builtin_bit_cast(float, c ? ua : ub);
+}
+
 // Values staged per node in LDS (field-major: value v of node t at v*NODES+t).
 // The three metric values Ja^k_1..3 of a node sit at kJa + 3k.
 enum NodeValue {
@@ -84,23 +139,43 @@ enum NodeValue {
 };
 constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 
-template <int N, int EPB, int NT>
+// Launch configuration of one kernel instance: EPB elements per workgroup of
+// NT threads; WAVES > 0 asks the compiler to fit at least WAVES waves per
+// SIMD (it then caps the registers); METRIC_LDS stages the metric terms in
+// LDS (coalesced loads in phase A) instead of loading them per line thread.
+template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
+          bool KMAJOR_ = false>
+struct LaunchCfg {
+    static constexpr int EPB = EPB_;
+    static constexpr int NT = NT_;
+    static constexpr int WAVES = WAVES_;
+    static constexpr bool kMetricInLds = METRIC_LDS_;
+    // CACHE: read the line's N+1 nodes from LDS once into registers (fewer
+    // LDS reads, more registers); otherwise stream them per pair.
+    static constexpr bool kCacheLine = CACHE_;
+    // KMAJOR: order line tasks direction-major (all direction-1 lines of the
+    // workgroup first), so each wave reads LDS with one stride pattern.
+    static constexpr bool kDirMajor = KMAJOR_;
+};
+
+template <int N, class C>
 struct Shape {
     static constexpr int Nq = N + 1;
     static constexpr int Nq2 = Nq * Nq;
     static constexpr int Np = Nq2 * Nq;
-    static constexpr int kNodes = EPB * Np;            // nodes per workgroup
-    static constexpr int kLines = 3 * EPB * Nq2;        // line tasks per workgroup
-    static constexpr int kLdsValues =
-        (kNodeValues > kPartialValues ? kNodeValues : kPartialValues) * kNodes;
-    static_assert(kLines <= NT, "one line task per thread");
+    static constexpr int kNodes = C::EPB * Np;          // nodes per workgroup
+    static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
+    static constexpr int kNodeIters = (kNodes + C::NT - 1) / C::NT;  // nodes per thread
+    static constexpr int kStaged = C::kMetricInLds ? kNodeValues : kJa;
+    static constexpr int kLdsValues = (kStaged > kPartialValues ? kStaged : kPartialValues) * kNodes;
+    static_assert(kLines <= C::NT, "one line task per thread");
 };
 
 // One node's staged values, read from LDS where a pair needs them.
 template <typename T>
 struct NodeRegs {
     T rho, u1, u2, u3, b, lrho, lb, ph, usq, ib, n1, n2, n3;
-    __device__ inline void load(const T *lds, int NODES, int s, int k) {
+    __device__ inline void load_state(const T *lds, int NODES, int s) {
         rho = lds[kRho * NODES + s];
         u1 = lds[kU1 * NODES + s];
         u2 = lds[kU2 * NODES + s];
@@ -111,177 +186,376 @@ struct NodeRegs {
         ph = lds[kPhi * NODES + s];
         usq = lds[kUsq * NODES + s];
         ib = lds[kInvB * NODES + s];
+    }
+    __device__ inline void load_metric(const T *lds, int NODES, int s, int k) {
         n1 = lds[(kJa + 3 * k + 0) * NODES + s];
         n2 = lds[(kJa + 3 * k + 1) * NODES + s];
         n3 = lds[(kJa + 3 * k + 2) * NODES + s];
     }
 };
 
-template <typename T, int N, int EPB, int NT>
-__global__ __launch_bounds__(NT) void volume_rhs_kernel(
-    const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
-    const T *__restrict__ D, int64_t nelem, T *__restrict__ rhs)
+// Contribution of the unordered pair (a, l) of one line, both directions of
+// the pair, added to the accumulators of nodes a and l.
+// X and Y are taken by value: a reference would take the address of the
+// caller's locals, and the compiler fence in the pair loop would then keep
+// them in scratch memory.  D[a][l] and D[l][a] are read where they are used.
+template <typename T>
+__device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
+                                   const T *__restrict__ Dal_p, const T *__restrict__ Dla_p,
+                                   T *acc_a, T *acc_l)
 {
-    using S = Shape<N, EPB, NT>;
     using A = Arith<T>;
-    constexpr int Nq = S::Nq, Nq2 = S::Nq2, Np = S::Np, NODES = S::kNodes;
-    __shared__ T lds[S::kLdsValues];
+    const T eps = T(A::kSeries);
+    const T lnk = T(A::kLogToLn);
+    const T cE = T(kBScale / (2.0 * (kGamma - 1.0)));  // s_b/(2(gamma-1))
+    const T half_bscale = T(0.5 * kBScale);
+    // sums and jumps (jumps are partner l minus receiving node a)
+    const T sr = X.rho + Y.rho, dr = Y.rho - X.rho;
+    const T sb = X.b + Y.b, db = Y.b - X.b;
+    const bool ser_r = dr * dr < eps * (sr * sr);
+    const bool ser_b = db * db < eps * (sb * sb);
+    // one reciprocal serves 1/sr, 1/sb, 1/(ln rho_l - ln rho_a), 1/db
+    const T Ar = select(ser_r, T(1), lnk * (Y.lrho - X.lrho));
+    const T Bb = select(ser_b, T(1), db);
+    const T srsb = sr * sb, AB = Ar * Bb;
+    const T R = A::rcp(srsb * AB);
+    const T isr = R * sb * AB;
+    const T isb = R * sr * AB;
+    const T iAr = R * srsb * Bb;
+    const T iBb = R * srsb * Ar;
+    // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference)
+    const T tr = dr * isr;
+    const T fr = tr * tr;
+    const T qr = fma(fma(fma(T(-44.0 / 945.0), fr, T(-4.0 / 45.0)), fr, T(-1.0 / 3.0)), fr, T(1));
+    const T Lr = select(ser_r, T(0.5) * sr * qr, dr * iAr);
+    // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
+    const T tb = db * isb;
+    const T fb = tb * tb;
+    const T pb = fma(fma(fma(T(1.0 / 7.0), fb, T(1.0 / 5.0)), fb, T(1.0 / 3.0)), fb, T(1));
+    const T iLb = select(ser_b, T(2) * pb * isb, lnk * (Y.lb - X.lb) * iBb);
+    // {{rho}}/(2{{b}}) with the b scaling undone
+    const T pt = half_bscale * sr * isb;
+    // metric of the pair: Ja^k(a) + Ja^k(l)
+    const T c1 = X.n1 + Y.n1, c2 = X.n2 + Y.n2, c3 = X.n3 + Y.n3;
+    const T s1 = X.u1 + Y.u1, s2 = X.u2 + Y.u2, s3 = X.u3 + Y.u3;
+    // contravariant density flux {{rho}}_log ({{u}} . c)
+    const T Fr = T(0.5) * Lr * (c1 * s1 + c2 * s2 + c3 * s3);
+    const T hF = T(0.5) * Fr;
+    // symmetric momentum part S~_m = F~rho {{u_m}} + c_m {{rho}}/(2{{b}})
+    const T S1 = fma(hF, s1, c1 * pt);
+    const T S2 = fma(hF, s2, c2 * pt);
+    const T S3 = fma(hF, s3, c3 * pt);
+    // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~
+    const T coef = fma(cE, iLb, fma(T(-0.25), X.usq + Y.usq, T(0.5) * (X.ph + Y.ph)));
+    const T FE = fma(coef, Fr, T(0.5) * (s1 * S1 + s2 * S2 + s3 * S3));
+    // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
+    const T g = T(0.25) * sb * Lr * (Y.ph - X.ph);
+    const T ga = g * X.ib;
+    const T gl = -g * Y.ib;
+    const T Dal = *Dal_p;
+    const T Dla = *Dla_p;
+    acc_a[0] = fma(Dal, Fr, acc_a[0]);
+    acc_l[0] = fma(Dla, Fr, acc_l[0]);
+    acc_a[1] = fma(Dal, fma(ga, c1, S1), acc_a[1]);
+    acc_l[1] = fma(Dla, fma(gl, c1, S1), acc_l[1]);
+    acc_a[2] = fma(Dal, fma(ga, c2, S2), acc_a[2]);
+    acc_l[2] = fma(Dla, fma(gl, c2, S2), acc_l[2]);
+    acc_a[3] = fma(Dal, fma(ga, c3, S3), acc_a[3]);
+    acc_l[3] = fma(Dla, fma(gl, c3, S3), acc_l[3]);
+    acc_a[4] = fma(Dal, FE, acc_a[4]);
+    acc_l[4] = fma(Dla, FE, acc_l[4]);
+}
 
-    const int64_t e0 = (int64_t)blockIdx.x * EPB;
-    const int64_t fstride = nelem * Np;  // distance between fields
-    const int64_t left = nelem - e0;
-    const int nvalid = (left < EPB ? (int)left : EPB) * Np;
-    const int64_t g0 = e0 * Np;          // first node of this workgroup
+// Per-thread view of one workgroup's batch of elements.
+template <int N, class C>
+struct Batch {
+    using S = Shape<N, C>;
+    int64_t g0;      // first node of the batch
+    int nvalid;      // nodes of the batch that exist (EPB * Np except at the tail)
+    __device__ inline Batch(int64_t batch, int64_t nelem) {
+        const int64_t e0 = batch * C::EPB;
+        const int64_t left = nelem - e0;
+        nvalid = (left < C::EPB ? (int)left : C::EPB) * S::Np;
+        g0 = e0 * S::Np;
+    }
+};
 
+// The line task of this thread in phase B (fixed for the kernel's lifetime).
+template <int N, class C>
+struct LineTask {
+    using S = Shape<N, C>;
+    int eb, k, nb, step;
+    __device__ inline LineTask() {
+        constexpr int Nq = S::Nq, Nq2 = S::Nq2, Np = S::Np;
+        const int task = threadIdx.x;
+        int line;
+        if constexpr (C::kDirMajor) {
+            k = task / (C::EPB * Nq2);
+            const int r = task - k * (C::EPB * Nq2);
+            eb = r / Nq2;
+            line = r - eb * Nq2;
+            if (k > 2) { k = 2; eb = C::EPB; }  // idle thread: marked inactive below
+        } else {
+            eb = task / (3 * Nq2);
+            const int r3 = task - eb * (3 * Nq2);
+            k = r3 / Nq2;
+            line = r3 - k * Nq2;
+        }
+        const int p1 = line % Nq, p2 = line / Nq;
+        const int base = (k == 0) ? Nq * (p1 + Nq * p2) : (k == 1) ? p1 + Nq2 * p2 : p1 + Nq * p2;
+        step = (k == 0) ? 1 : (k == 1) ? Nq : Nq2;
+        nb = eb * Np + base;  // LDS index of the line's first node
+    }
+    __device__ inline bool active(int nvalid) const {
+        return (int)threadIdx.x < S::kLines && eb * S::Np < nvalid;
+    }
+};
+
+// Global values one thread loads for phase A: IT nodes x (5 fields, phi,
+// 9 metric terms when staged, J).
+template <typename T, int N, class C>
+struct NodeLoads {
+    using S = Shape<N, C>;
+    static constexpr int IT = S::kNodeIters;
+    T v[IT][6];
+    T m[C::kMetricInLds ? IT : 1][9];
+    T J[IT];
+    __device__ inline void issue(const T *__restrict__ q, const T *__restrict__ phi,
+                                 const T *__restrict__ geom, int64_t fstride, const Batch<N, C> &B) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int t = threadIdx.x + it * C::NT;
+            if (t < B.nvalid) {
+                const int64_t g = B.g0 + t;
+#pragma unroll
+                for (int f = 0; f < 5; ++f) v[it][f] = q[f * fstride + g];
+                v[it][5] = phi[g];
+                if constexpr (C::kMetricInLds) {
+#pragma unroll
+                    for (int j = 0; j < 9; ++j) m[it][j] = geom[j * fstride + g];
+                }
+                J[it] = geom[9 * fstride + g];
+            }
+        }
+    }
+};
+
+// Phase A compute: per-node primitives and logs into LDS; returns -1/J per node.
+template <typename T, int N, class C>
+__device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C> &B, T *lds,
+                                   T (&mJ)[Shape<N, C>::kNodeIters])
+{
+    using A = Arith<T>;
+    constexpr int NODES = Shape<N, C>::kNodes;
     const T gm1 = T(kGamma - 1.0);
     const T bscale = T(kBScale);
-
-    // ---- phase A: per-node primitives and logs, metric terms --------------
-    for (int t = threadIdx.x; t < nvalid; t += NT) {
-        const int64_t g = g0 + t;
-        const T rho = q[g];
-        const T m1 = q[fstride + g];
-        const T m2 = q[2 * fstride + g];
-        const T m3 = q[3 * fstride + g];
-        const T E = q[4 * fstride + g];
-        const T ph = phi[g];
-        const T irho = T(1) / rho;
-        const T u1 = m1 * irho, u2 = m2 * irho, u3 = m3 * irho;
-        const T usq = u1 * u1 + u2 * u2 + u3 * u3;
-        const T p = gm1 * (E - T(0.5) * rho * usq - rho * ph);
-        const T ip = T(1) / p;
-        const T b = T(0.5) * bscale * rho * ip;            // s_b rho/(2p)
-        const T ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
-        lds[kRho * NODES + t] = rho;
-        lds[kU1 * NODES + t] = u1;
-        lds[kU2 * NODES + t] = u2;
-        lds[kU3 * NODES + t] = u3;
-        lds[kB * NODES + t] = b;
-        lds[kLogRho * NODES + t] = A::node_log(rho);
-        lds[kLogB * NODES + t] = A::node_log(b);
-        lds[kPhi * NODES + t] = ph;
-        lds[kUsq * NODES + t] = usq;
-        lds[kInvB * NODES + t] = ib;
 #pragma unroll
-        for (int m = 0; m < 9; ++m) lds[(kJa + m) * NODES + t] = geom[m * fstride + g];
+    for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
+        const int t = threadIdx.x + it * C::NT;
+        if (t < B.nvalid) {
+            const T rho = L.v[it][0], E = L.v[it][4], ph = L.v[it][5];
+            const T m1 = L.v[it][1], m2 = L.v[it][2], m3 = L.v[it][3];
+            const T irho = A::rcp(rho);
+            const T u1 = m1 * irho, u2 = m2 * irho, u3 = m3 * irho;
+            const T usq = u1 * u1 + u2 * u2 + u3 * u3;
+            const T p = gm1 * (E - T(0.5) * (m1 * u1 + m2 * u2 + m3 * u3) - rho * ph);
+            const T b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
+            const T ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
+            lds[kRho * NODES + t] = rho;
+            lds[kU1 * NODES + t] = u1;
+            lds[kU2 * NODES + t] = u2;
+            lds[kU3 * NODES + t] = u3;
+            lds[kB * NODES + t] = b;
+            lds[kLogRho * NODES + t] = A::node_log(rho);
+            lds[kLogB * NODES + t] = A::node_log(b);
+            lds[kPhi * NODES + t] = ph;
+            lds[kUsq * NODES + t] = usq;
+            lds[kInvB * NODES + t] = ib;
+            if constexpr (C::kMetricInLds) {
+#pragma unroll
+                for (int j = 0; j < 9; ++j) lds[(kJa + j) * NODES + t] = L.m[it][j];
+            }
+            mJ[it] = -A::rcp(L.J[it]);
+        }
     }
+}
+
+// Phase B: every unordered pair of this thread's line.
+template <typename T, int N, class C>
+__device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const LineTask<N, C> &L,
+                                  const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
+                                  T (&acc)[N + 1][5])
+{
+    constexpr int Nq = N + 1, NODES = Shape<N, C>::kNodes;
+    if constexpr (C::kCacheLine) {
+        NodeRegs<T> V[Nq];
+#pragma unroll
+        for (int a = 0; a < Nq; ++a) {
+            V[a].load_state(lds, NODES, L.nb + a * L.step);
+            if constexpr (C::kMetricInLds) {
+                V[a].load_metric(lds, NODES, L.nb + a * L.step, L.k);
+            } else {
+                V[a].n1 = lm[a][0]; V[a].n2 = lm[a][1]; V[a].n3 = lm[a][2];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < Nq - 1; ++a)
+#pragma unroll
+            for (int l = a + 1; l < Nq; ++l)
+                pair_update(V[a], V[l], D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+        return;
+    }
+#pragma unroll
+    for (int a = 0; a < Nq - 1; ++a) {
+        // Re-read node values from LDS in every outer iteration instead of
+        // keeping the whole line live in registers.
+        asm volatile("" ::: "memory");
+        NodeRegs<T> X;
+        X.load_state(lds, NODES, L.nb + a * L.step);
+        if constexpr (C::kMetricInLds) {
+            X.load_metric(lds, NODES, L.nb + a * L.step, L.k);
+        } else {
+            X.n1 = lm[a][0]; X.n2 = lm[a][1]; X.n3 = lm[a][2];
+        }
+#pragma unroll
+        for (int l = a + 1; l < Nq; ++l) {
+            NodeRegs<T> Y;
+            Y.load_state(lds, NODES, L.nb + l * L.step);
+            if constexpr (C::kMetricInLds) {
+                Y.load_metric(lds, NODES, L.nb + l * L.step, L.k);
+            } else {
+                Y.n1 = lm[l][0]; Y.n2 = lm[l][1]; Y.n3 = lm[l][2];
+            }
+            pair_update(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+        }
+    }
+}
+
+// Phases C and D: directional partials through LDS, scaling, store.
+template <typename T, int N, class C>
+__device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool active,
+                                      const T (&acc)[N + 1][5])
+{
+    constexpr int NODES = Shape<N, C>::kNodes;
+    if (active) {
+#pragma unroll
+        for (int a = 0; a < N + 1; ++a) {
+            const int s = L.nb + a * L.step;
+#pragma unroll
+            for (int f = 0; f < 5; ++f) lds[(L.k * 5 + f) * NODES + s] = acc[a][f];
+        }
+    }
+}
+
+template <typename T, int N, class C>
+__device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fstride,
+                                 const T (&mJ)[Shape<N, C>::kNodeIters], T *__restrict__ rhs)
+{
+    constexpr int NODES = Shape<N, C>::kNodes;
+#pragma unroll
+    for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
+        const int t = threadIdx.x + it * C::NT;
+        if (t < B.nvalid) {
+            const int64_t g = B.g0 + t;
+#pragma unroll
+            for (int f = 0; f < 5; ++f) {
+                const T s = lds[f * NODES + t] + lds[(5 + f) * NODES + t] + lds[(10 + f) * NODES + t];
+                rhs[f * fstride + g] = s * mJ[it];
+            }
+        }
+    }
+}
+
+// One workgroup per batch of EPB elements.
+template <typename T, int N, class C>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
+__attribute__((amdgpu_waves_per_eu(C::WAVES > 0 ? C::WAVES : 1)))
+volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
+                  const T *__restrict__ D, int64_t nelem, T *__restrict__ rhs)
+{
+    using S = Shape<N, C>;
+    constexpr int Nq = N + 1;
+    __shared__ T lds[S::kLdsValues];
+    const int64_t fstride = nelem * S::Np;
+    const Batch<N, C> B(blockIdx.x, nelem);
+    const LineTask<N, C> L;
+    const bool active = L.active(B.nvalid);
+
+    // phase A: issue every global load first
+    NodeLoads<T, N, C> ld;
+    ld.issue(q, phi, geom, fstride, B);
+    T lm[C::kMetricInLds ? 1 : Nq][3];
+    if constexpr (!C::kMetricInLds) {
+        if (active) {
+#pragma unroll
+            for (int a = 0; a < Nq; ++a)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    lm[a][j] = geom[(3 * L.k + j) * fstride + B.g0 + L.nb + a * L.step];
+        }
+    }
+    T mJ[S::kNodeIters];
+    stage_nodes<T, N, C>(ld, B, lds, mJ);
     __syncthreads();
 
-    // ---- phase B: one thread per grid line ---------------------------------
-    const int task = threadIdx.x;
-    const int eb = task / (3 * Nq2);
-    const int r3 = task - eb * (3 * Nq2);
-    const int k = r3 / Nq2;
-    const int line = r3 - k * Nq2;
-    const int p1 = line % Nq, p2 = line / Nq;
-    const int base = (k == 0) ? Nq * (p1 + Nq * p2) : (k == 1) ? p1 + Nq2 * p2 : p1 + Nq * p2;
-    const int step = (k == 0) ? 1 : (k == 1) ? Nq : Nq2;
-    const bool active = (task < S::kLines) && (eb * Np < nvalid);
-    const int nb = eb * Np + base;  // LDS index of the line's first node
-
+    // phase B
     T acc[Nq][5];
 #pragma unroll
     for (int a = 0; a < Nq; ++a)
 #pragma unroll
         for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
-
-    if (active) {
-        const T eps = T(A::kSeries);
-        const T lnk = T(A::kLogToLn);
-        const T cE = T(kBScale / (2.0 * (kGamma - 1.0)));  // s_b/(2(gamma-1))
-        const T half_bscale = T(0.5 * kBScale);
-
-#pragma unroll
-        for (int a = 0; a < Nq - 1; ++a) {
-            // Re-read node values from LDS in every outer iteration instead of
-            // keeping the whole line live in registers.
-            asm volatile("" ::: "memory");
-            NodeRegs<T> X;
-            X.load(lds, NODES, nb + a * step, k);
-#pragma unroll
-            for (int l = a + 1; l < Nq; ++l) {
-                NodeRegs<T> Y;
-                Y.load(lds, NODES, nb + l * step, k);
-                // sums and jumps (jumps are partner l minus receiving node a)
-                const T sr = X.rho + Y.rho, dr = Y.rho - X.rho;
-                const T sb = X.b + Y.b, db = Y.b - X.b;
-                const bool ser_r = dr * dr < eps * (sr * sr);
-                const bool ser_b = db * db < eps * (sb * sb);
-                // one reciprocal serves 1/sr, 1/sb, 1/(ln rho_l - ln rho_a), 1/db
-                const T Ar = ser_r ? T(1) : lnk * (Y.lrho - X.lrho);
-                const T Bb = ser_b ? T(1) : db;
-                const T srsb = sr * sb, AB = Ar * Bb;
-                const T R = A::rcp(srsb * AB);
-                const T isr = R * sb * AB;
-                const T isb = R * sr * AB;
-                const T iAr = R * srsb * Bb;
-                const T iBb = R * srsb * Ar;
-                // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference)
-                const T tr = dr * isr;
-                const T fr = tr * tr;
-                const T qr = fma(fma(fma(T(-44.0 / 945.0), fr, T(-4.0 / 45.0)), fr, T(-1.0 / 3.0)), fr, T(1));
-                const T Lr = ser_r ? T(0.5) * sr * qr : dr * iAr;
-                // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
-                const T tb = db * isb;
-                const T fb = tb * tb;
-                const T pb = fma(fma(fma(T(1.0 / 7.0), fb, T(1.0 / 5.0)), fb, T(1.0 / 3.0)), fb, T(1));
-                const T iLb = ser_b ? T(2) * pb * isb : lnk * (Y.lb - X.lb) * iBb;
-                // {{rho}}/(2{{b}}) with the b scaling undone
-                const T pt = half_bscale * sr * isb;
-                // metric of the pair: Ja^k(a) + Ja^k(l)
-                const T c1 = X.n1 + Y.n1, c2 = X.n2 + Y.n2, c3 = X.n3 + Y.n3;
-                const T s1 = X.u1 + Y.u1, s2 = X.u2 + Y.u2, s3 = X.u3 + Y.u3;
-                // contravariant density flux {{rho}}_log ({{u}} . c)
-                const T Fr = T(0.5) * Lr * (c1 * s1 + c2 * s2 + c3 * s3);
-                const T hF = T(0.5) * Fr;
-                // symmetric momentum part S~_m = F~rho {{u_m}} + c_m {{rho}}/(2{{b}})
-                const T S1 = fma(hF, s1, c1 * pt);
-                const T S2 = fma(hF, s2, c2 * pt);
-                const T S3 = fma(hF, s3, c3 * pt);
-                // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~
-                const T coef = fma(cE, iLb, fma(T(-0.25), X.usq + Y.usq, T(0.5) * (X.ph + Y.ph)));
-                const T FE = fma(coef, Fr, T(0.5) * (s1 * S1 + s2 * S2 + s3 * S3));
-                // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
-                const T g = T(0.25) * sb * Lr * (Y.ph - X.ph);
-                const T ga = g * X.ib;
-                const T gl = -g * Y.ib;
-                const T Dal = D[a * Nq + l];
-                const T Dla = D[l * Nq + a];
-                acc[a][0] = fma(Dal, Fr, acc[a][0]);
-                acc[l][0] = fma(Dla, Fr, acc[l][0]);
-                acc[a][1] = fma(Dal, fma(ga, c1, S1), acc[a][1]);
-                acc[l][1] = fma(Dla, fma(gl, c1, S1), acc[l][1]);
-                acc[a][2] = fma(Dal, fma(ga, c2, S2), acc[a][2]);
-                acc[l][2] = fma(Dla, fma(gl, c2, S2), acc[l][2]);
-                acc[a][3] = fma(Dal, fma(ga, c3, S3), acc[a][3]);
-                acc[l][3] = fma(Dla, fma(gl, c3, S3), acc[l][3]);
-                acc[a][4] = fma(Dal, FE, acc[a][4]);
-                acc[l][4] = fma(Dla, FE, acc[l][4]);
-            }
-        }
-    }
+    if (active) line_pairs<T, N, C>(lds, D, L, lm, acc);
     __syncthreads();  // node values are dead from here on: LDS becomes the partials
 
-    // ---- phase C: directional partial sums to LDS --------------------------
-    if (active) {
-#pragma unroll
-        for (int a = 0; a < Nq; ++a) {
-            const int s = nb + a * step;
-#pragma unroll
-            for (int f = 0; f < 5; ++f) lds[(k * 5 + f) * NODES + s] = acc[a][f];
-        }
-    }
+    // phases C, D
+    write_partials<T, N, C>(lds, L, active, acc);
     __syncthreads();
+    store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
+}
 
-    // ---- phase D: sum directions, scale by -1/J, store -------------------
-    for (int t = threadIdx.x; t < nvalid; t += NT) {
-        const int64_t g = g0 + t;
-        const T mJ = T(-1) / geom[9 * fstride + g];
+// Persistent variant: the grid holds only resident workgroups; each walks
+// batches blockIdx.x, blockIdx.x + gridDim.x, ... and loads the next batch's
+// node data into registers while it evaluates the pairs of the current one,
+// so HBM traffic overlaps the pair arithmetic.
+template <typename T, int N, class C>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
+__attribute__((amdgpu_waves_per_eu(C::WAVES > 0 ? C::WAVES : 1)))
+volume_rhs_persistent(const T *__restrict__ q, const T *__restrict__ phi,
+                      const T *__restrict__ geom, const T *__restrict__ D, int64_t nelem,
+                      T *__restrict__ rhs)
+{
+    static_assert(C::kMetricInLds, "the persistent kernel stages the metric in LDS");
+    using S = Shape<N, C>;
+    constexpr int Nq = N + 1;
+    __shared__ T lds[S::kLdsValues];
+    const int64_t fstride = nelem * S::Np;
+    const int64_t nbatch = (nelem + C::EPB - 1) / C::EPB;
+    const LineTask<N, C> L;
+    const T lm[1][3] = {{T(0), T(0), T(0)}};
+
+    int64_t batch = blockIdx.x;  // uniform over the workgroup: whole workgroups exit
+    NodeLoads<T, N, C> ld;
+    if (batch < nbatch) ld.issue(q, phi, geom, fstride, Batch<N, C>(batch, nelem));
+    for (; batch < nbatch; batch += gridDim.x) {
+        const Batch<N, C> B(batch, nelem);
+        const bool active = L.active(B.nvalid);
+        T mJ[S::kNodeIters];
+        stage_nodes<T, N, C>(ld, B, lds, mJ);
+        __syncthreads();
+        const int64_t next = batch + gridDim.x;
+        if (next < nbatch) ld.issue(q, phi, geom, fstride, Batch<N, C>(next, nelem));
+
+        T acc[Nq][5];
 #pragma unroll
-        for (int f = 0; f < 5; ++f) {
-            const T s = lds[f * NODES + t] + lds[(5 + f) * NODES + t] + lds[(10 + f) * NODES + t];
-            rhs[f * fstride + g] = s * mJ;
-        }
+        for (int a = 0; a < Nq; ++a)
+#pragma unroll
+            for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
+        if (active) line_pairs<T, N, C>(lds, D, L, lm, acc);
+        __syncthreads();
+        write_partials<T, N, C>(lds, L, active, acc);
+        __syncthreads();
+        store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
+        __syncthreads();  // partials read before the next batch's node values overwrite them
     }
 }
 

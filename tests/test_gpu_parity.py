@@ -118,6 +118,32 @@ def test_every_order_random_state(N, dtype):
     check(got, ref, TOL[dtype], f"random N={N} {np.dtype(dtype).name}")
 
 
+@pytest.mark.parametrize("N", [3, 4, 7])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_log_branch_stress(N, dtype):
+    """Node-by-node random states spanning decades (rho in [1e-3, 1e3],
+    T in [50, 5000] K so b = 1/(2RT) spans two decades, p = rho R T,
+    |u| <= 100 m/s, phi in [0, 3e5]): nearly every pair takes the
+    log-difference branch of both log means, over a wide range of magnitudes.
+    rho phi / p stays below ~21, so recovering p from E is well conditioned
+    in both precisions."""
+    rng = np.random.default_rng(100 + N)
+    D = I.diff_matrix(N)
+    X = I.box_mesh((2, 2, 1), (0, 0, 0), (2000, 2000, 1000), N, warp_frac=0.05, seed=N,
+                   warp_wavelength=(1000, 1000, 1000))
+    geom = I.metrics(X, D)
+    shape = geom[0].shape
+    rho = 10.0 ** rng.uniform(-3, 3, shape)
+    p = rho * I.R_GAS * 10.0 ** rng.uniform(np.log10(50.0), np.log10(5000.0), shape)
+    u = rng.uniform(-100, 100, (3,) + shape)
+    phi = rng.uniform(0, 3e5, shape)
+    q = I.conserved(rho, u, p, phi)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_rhs(q, phi, geom, D)
+    ref = oracle.volume_rhs(q, phi, geom, D, N)
+    check(got, ref, TOL[dtype], f"log-branch stress N={N} {np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("nelem", [1, 3, 5, 7, 4093])
 def test_ragged_element_counts(workloads, nelem):
     """Element counts that leave the last workgroup partly empty."""

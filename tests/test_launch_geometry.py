@@ -19,13 +19,23 @@ PARTIAL_VALUES = 15  # 3 directions x 5 fields
 
 
 def launch_table():
+    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major)} parsed from esdg_api.hip."""
     text = open(API).read()
-    rows = re.findall(r"struct Launch<(\d+)>\s*\{\s*static constexpr int EPB = (\d+), NT = (\d+);", text)
-    return {int(n): (int(e), int(t)) for n, e, t in rows}
+    rows = re.findall(r"struct Launch<(double|float), (\d+)>\s*\{\s*using C = LaunchCfg<([^>]*)>;", text)
+    table = {}
+    for dt, n, args in rows:
+        parts = [a.strip() for a in args.split(",")]
+        epb, nt = int(parts[0]), int(parts[1])
+        metric = parts[3] != "false" if len(parts) > 3 else True
+        dirmajor = parts[5] == "true" if len(parts) > 5 else False
+        table[(dt, int(n))] = (epb, nt, metric, dirmajor)
+    return table
 
 
 def test_launch_table_covers_orders():
-    assert sorted(launch_table()) == list(range(1, 9))
+    t = launch_table()
+    assert sorted(n for d, n in t if d == "double") == list(range(1, 9))
+    assert sorted(n for d, n in t if d == "float") == list(range(1, 9))
 
 
 def test_staged_value_count_matches_kernel():
@@ -37,16 +47,19 @@ def test_staged_value_count_matches_kernel():
     assert names.index("kJa") + 9 == NODE_VALUES
 
 
+@pytest.mark.parametrize("dtype", ["double", "float"])
 @pytest.mark.parametrize("N", range(1, 9))
 @pytest.mark.parametrize("nelem", [1, 2, 5, 13])
-def test_indices_in_bounds(N, nelem):
-    EPB, NT = launch_table()[N]
+def test_indices_in_bounds(dtype, N, nelem):
+    EPB, NT, metric_in_lds, dirmajor = launch_table()[(dtype, N)]
     Nq = N + 1
     Nq2, Np = Nq * Nq, Nq ** 3
     NODES = EPB * Np
-    lds_values = max(NODE_VALUES, PARTIAL_VALUES) * NODES
+    staged = NODE_VALUES if metric_in_lds else 10
+    lds_values = max(staged, PARTIAL_VALUES) * NODES
     lines = 3 * EPB * Nq2
     assert lines <= NT
+    node_iters = (NODES + NT - 1) // NT
     blocks = (nelem + EPB - 1) // EPB
     fstride = nelem * Np
     written = np.zeros((3, nelem * Np), dtype=int)
@@ -55,20 +68,31 @@ def test_indices_in_bounds(N, nelem):
         e0 = blk * EPB
         nvalid = min(EPB, nelem - e0) * Np
         g0 = e0 * Np
-        # phase A / D: node threads
+        # phase A / D: node threads, node_iters nodes each
         for t in range(NT):
-            for tt in range(t, nvalid, NT):
+            for it in range(node_iters):
+                tt = t + it * NT
+                if tt >= nvalid:
+                    continue
                 g = g0 + tt
                 assert 0 <= g and 4 * fstride + g < 5 * fstride and 9 * fstride + g < 10 * fstride
-                assert (NODE_VALUES - 1) * NODES + tt < lds_values
+                assert (staged - 1) * NODES + tt < lds_values
                 assert (10 + 4) * NODES + tt < lds_values
                 out_written[g] += 1
         # phase B / C: line threads
         for task in range(NT):
-            eb = task // (3 * Nq2)
-            r3 = task - eb * 3 * Nq2
-            k = r3 // Nq2
-            line = r3 - k * Nq2
+            if dirmajor:
+                k = task // (EPB * Nq2)
+                r = task - k * EPB * Nq2
+                eb = r // Nq2
+                line = r - eb * Nq2
+                if k > 2:
+                    k, eb = 2, EPB
+            else:
+                eb = task // (3 * Nq2)
+                r3 = task - eb * 3 * Nq2
+                k = r3 // Nq2
+                line = r3 - k * Nq2
             p1, p2 = line % Nq, line // Nq
             base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
             step = [1, Nq, Nq2][k]
@@ -79,7 +103,11 @@ def test_indices_in_bounds(N, nelem):
             for a in range(Nq):
                 s = nb + a * step
                 assert eb * Np <= s < (eb + 1) * Np <= NODES
-                assert (10 + 3 * k + 2) * NODES + s < lds_values   # staged reads
+                if metric_in_lds:
+                    assert (10 + 3 * k + 2) * NODES + s < lds_values   # staged reads
+                else:
+                    assert (3 * k + 2) * fstride + g0 + s < 9 * fstride  # direct metric loads
+                assert 9 * NODES + s < lds_values
                 assert (k * 5 + 4) * NODES + s < lds_values         # partial writes
                 written[k, g0 + s] += 1
                 for l in range(a + 1, Nq):
