@@ -23,7 +23,7 @@ template <typename T, int N> struct Launch;
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false>; };              // 192/192
-template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, true, true>; };  // 225/256
+template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true>; }; // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128>; };                        // 108/128
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192>; };                        // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true>; }; // 192/192

@@ -90,9 +90,10 @@ __device__ inline double ln_pos(double x)
 }
 
 template <> struct Arith<double> {
-    // series branch of the log mean when f = ((c-a)/(c+a))^2 < kSeries:
-    // truncation after f^3 leaves an error below f^4/9 < 2e-17.
-    static constexpr double kSeries = 1.0e-4;
+    // series branch of the log mean when |c-a| < kSeries (c+a), i.e.
+    // f = ((c-a)/(c+a))^2 < 1e-4: truncation after f^3 leaves an error below
+    // f^4/9 < 2e-17.
+    static constexpr double kSeries = 1.0e-2;
     // node logs are natural logs
     static constexpr double kLogToLn = 1.0;
     __device__ static inline double node_log(double x) { return ln_pos(x); }
@@ -107,8 +108,9 @@ template <> struct Arith<double> {
 };
 
 template <> struct Arith<float> {
-    // f < 1e-2: truncation after f^3 leaves an error below 1.2e-9
-    static constexpr float kSeries = 1.0e-2f;
+    // |c-a| < 0.1 (c+a), f < 1e-2: truncation after f^3 leaves an error
+    // below 1.2e-9
+    static constexpr float kSeries = 1.0e-1f;
     // node logs are base-2 logs (hardware v_log_f32); ln x = ln2 * log2 x
     static constexpr float kLogToLn = 0.693147180559945309f;
     __device__ static inline float node_log(float x) { return __builtin_amdgcn_logf(x); }
@@ -212,8 +214,8 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     // sums and jumps (jumps are partner l minus receiving node a)
     const T sr = X.rho + Y.rho, dr = Y.rho - X.rho;
     const T sb = X.b + Y.b, db = Y.b - X.b;
-    const bool ser_r = dr * dr < eps * (sr * sr);
-    const bool ser_b = db * db < eps * (sb * sb);
+    const bool ser_r = fabs(dr) < eps * sr;
+    const bool ser_b = fabs(db) < eps * sb;
     // one reciprocal serves 1/sr, 1/sb, 1/(ln rho_l - ln rho_a), 1/db
     const T Ar = select(ser_r, T(1), lnk * (Y.lrho - X.lrho));
     const T Bb = select(ser_b, T(1), db);
@@ -223,16 +225,18 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     const T isb = R * sr * AB;
     const T iAr = R * srsb * Bb;
     const T iBb = R * srsb * Ar;
-    // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference)
+    // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference);
+    // s/atanh(s) = 1 - f/3 - 4f^2/45 - 44f^3/945 - ..., f = s^2, halved here
     const T tr = dr * isr;
     const T fr = tr * tr;
-    const T qr = fma(fma(fma(T(-44.0 / 945.0), fr, T(-4.0 / 45.0)), fr, T(-1.0 / 3.0)), fr, T(1));
-    const T Lr = select(ser_r, T(0.5) * sr * qr, dr * iAr);
-    // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
+    const T qr = fma(fma(fma(T(-22.0 / 945.0), fr, T(-2.0 / 45.0)), fr, T(-1.0 / 6.0)), fr, T(0.5));
+    const T Lr = select(ser_r, sr * qr, dr * iAr);
+    // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db;
+    // atanh(s)/s = 1 + f/3 + f^2/5 + f^3/7 + ..., doubled here
     const T tb = db * isb;
     const T fb = tb * tb;
-    const T pb = fma(fma(fma(T(1.0 / 7.0), fb, T(1.0 / 5.0)), fb, T(1.0 / 3.0)), fb, T(1));
-    const T iLb = select(ser_b, T(2) * pb * isb, lnk * (Y.lb - X.lb) * iBb);
+    const T pb = fma(fma(fma(T(2.0 / 7.0), fb, T(2.0 / 5.0)), fb, T(2.0 / 3.0)), fb, T(2));
+    const T iLb = select(ser_b, pb * isb, lnk * (Y.lb - X.lb) * iBb);
     // {{rho}}/(2{{b}}) with the b scaling undone
     const T pt = half_bscale * sr * isb;
     // metric of the pair: Ja^k(a) + Ja^k(l)
