@@ -19,14 +19,14 @@ constexpr int kMaxOrder = 8;
 // timing on MI355X at the bubble, baroclinic and N=4 L=6 mesh sizes.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
-// registers, direction-major line order>
+// registers, direction-major line order, direction-3 lines finish the nodes>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false>; };              // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true>; }; // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128>; };                        // 108/128
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192>; };                        // 147/192
-template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true>; }; // 192/192
+template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true>; }; // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256>; };                        // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };

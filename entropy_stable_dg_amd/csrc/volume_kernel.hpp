@@ -56,7 +56,8 @@ template <typename T> struct Arith;
 // s^23 (remainder below 2e-19 relative); e ln2 is added in two parts (ln2 split
 // into a 32-bit head and a tail) so e ln2_hi is exact.  Absolute error is a
 // few ulp of |ln x|; only differences of two such logs larger than ~0.02 are
-// used, so this is ample.
+// used, so this is ample (the division by m+1 carries a relative error below
+// 3e-15, i.e. below 1e-15 absolute in ln m).
 __device__ inline double ln_pos(double x)
 {
     int e;
@@ -67,8 +68,7 @@ __device__ inline double ln_pos(double x)
     }
     const double num = m - 1.0, den = m + 1.0;
     double r = __builtin_amdgcn_rcp(den);
-    r = fma(r, fma(-den, r, 1.0), r);
-    r = fma(r, fma(-den, r, 1.0), r);
+    r = fma(r, fma(-den, r, 1.0), r);     // one Newton step: relative error < 3e-15
     const double t = num * r;
     const double t2 = t * t;
     double p = 1.0 / 23.0;
@@ -97,13 +97,12 @@ template <> struct Arith<double> {
     // node logs are natural logs
     static constexpr double kLogToLn = 1.0;
     __device__ static inline double node_log(double x) { return ln_pos(x); }
-    // 1/x: hardware estimate refined by two Newton steps (error ~1 ulp)
+    // 1/x: the hardware estimate (relative error below 5e-8 on gfx950)
+    // refined by one Newton step, which squares the error: below 3e-15,
+    // far inside the 1e-11 the volume term is held to.
     __device__ static inline double rcp(double x) {
-        double r = __builtin_amdgcn_rcp(x);
-        double e = fma(-x, r, 1.0);
-        r = fma(r, e, r);
-        e = fma(-x, r, 1.0);
-        return fma(r, e, r);
+        const double r = __builtin_amdgcn_rcp(x);
+        return fma(r, fma(-x, r, 1.0), r);
     }
 };
 
@@ -134,9 +133,10 @@ __device__ inline float select(bool c, float a, float b)
 }
 
 // Values staged per node in LDS (field-major: value v of node t at v*NODES+t).
+// kW holds w = phi - |u|^2/2 (the energy flux needs only the pair mean of w).
 // The three metric values Ja^k_1..3 of a node sit at kJa + 3k.
 enum NodeValue {
-    kRho = 0, kU1, kU2, kU3, kB, kLogRho, kLogB, kPhi, kUsq, kInvB, kJa,
+    kRho = 0, kU1, kU2, kU3, kB, kLogRho, kLogB, kPhi, kW, kInvB, kJa,
     kNodeValues = kJa + 9
 };
 constexpr int kPartialValues = 15;  // 3 directions x 5 fields
@@ -146,7 +146,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 // SIMD (it then caps the registers); METRIC_LDS stages the metric terms in
 // LDS (coalesced loads in phase A) instead of loading them per line thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
-          bool KMAJOR_ = false>
+          bool KMAJOR_ = false, bool FIN_ = false>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -158,6 +158,10 @@ struct LaunchCfg {
     // KMAJOR: order line tasks direction-major (all direction-1 lines of the
     // workgroup first), so each wave reads LDS with one stride pattern.
     static constexpr bool kDirMajor = KMAJOR_;
+    // FIN: the direction-3 line threads finish their own nodes (adding the
+    // two other directions' partials from LDS, scaling by -1/J, storing), so
+    // LDS holds two directional partials instead of three.
+    static constexpr bool kFinalizeInLine = FIN_;
 };
 
 template <int N, class C>
@@ -169,14 +173,18 @@ struct Shape {
     static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
     static constexpr int kNodeIters = (kNodes + C::NT - 1) / C::NT;  // nodes per thread
     static constexpr int kStaged = C::kMetricInLds ? kNodeValues : kJa;
-    static constexpr int kLdsValues = (kStaged > kPartialValues ? kStaged : kPartialValues) * kNodes;
+    static constexpr int kPartials = C::kFinalizeInLine ? 10 : kPartialValues;
+    static constexpr int kRegion = kStaged > kPartials ? kStaged : kPartials;
+    // with FIN, -1/J of every node is staged after the shared region
+    static constexpr int kMinusInvJ = kRegion;
+    static constexpr int kLdsValues = (kRegion + (C::kFinalizeInLine ? 1 : 0)) * kNodes;
     static_assert(kLines <= C::NT, "one line task per thread");
 };
 
 // One node's staged values, read from LDS where a pair needs them.
 template <typename T>
 struct NodeRegs {
-    T rho, u1, u2, u3, b, lrho, lb, ph, usq, ib, n1, n2, n3;
+    T rho, u1, u2, u3, b, lrho, lb, ph, w, ib, n1, n2, n3;
     __device__ inline void load_state(const T *lds, int NODES, int s) {
         rho = lds[kRho * NODES + s];
         u1 = lds[kU1 * NODES + s];
@@ -186,7 +194,7 @@ struct NodeRegs {
         lrho = lds[kLogRho * NODES + s];
         lb = lds[kLogB * NODES + s];
         ph = lds[kPhi * NODES + s];
-        usq = lds[kUsq * NODES + s];
+        w = lds[kW * NODES + s];
         ib = lds[kInvB * NODES + s];
     }
     __device__ inline void load_metric(const T *lds, int NODES, int s, int k) {
@@ -249,8 +257,9 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     const T S1 = fma(hF, s1, c1 * pt);
     const T S2 = fma(hF, s2, c2 * pt);
     const T S3 = fma(hF, s3, c3 * pt);
-    // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~
-    const T coef = fma(cE, iLb, fma(T(-0.25), X.usq + Y.usq, T(0.5) * (X.ph + Y.ph)));
+    // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~,
+    // with -{{|u|^2}}/2 + {{phi}} = {{w}}
+    const T coef = fma(cE, iLb, T(0.5) * (X.w + Y.w));
     const T FE = fma(coef, Fr, T(0.5) * (s1 * S1 + s2 * S2 + s3 * S3));
     // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
     const T g = T(0.25) * sb * Lr * (Y.ph - X.ph);
@@ -373,13 +382,14 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
             lds[kLogRho * NODES + t] = A::node_log(rho);
             lds[kLogB * NODES + t] = A::node_log(b);
             lds[kPhi * NODES + t] = ph;
-            lds[kUsq * NODES + t] = usq;
+            lds[kW * NODES + t] = ph - T(0.5) * usq;
             lds[kInvB * NODES + t] = ib;
             if constexpr (C::kMetricInLds) {
 #pragma unroll
                 for (int j = 0; j < 9; ++j) lds[(kJa + j) * NODES + t] = L.m[it][j];
             }
             mJ[it] = -A::rcp(L.J[it]);
+            if constexpr (C::kFinalizeInLine) lds[Shape<N, C>::kMinusInvJ * NODES + t] = mJ[it];
         }
     }
 }
@@ -441,12 +451,33 @@ __device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool acti
                                       const T (&acc)[N + 1][5])
 {
     constexpr int NODES = Shape<N, C>::kNodes;
-    if (active) {
+    if (active && (!C::kFinalizeInLine || L.k < 2)) {
 #pragma unroll
         for (int a = 0; a < N + 1; ++a) {
             const int s = L.nb + a * L.step;
 #pragma unroll
             for (int f = 0; f < 5; ++f) lds[(L.k * 5 + f) * NODES + s] = acc[a][f];
+        }
+    }
+}
+
+// FIN: a direction-3 line thread adds the direction-1 and -2 partials of its
+// nodes to its own (same order as store_rhs), scales by -1/J and stores.
+template <typename T, int N, class C>
+__device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool active,
+                                   const Batch<N, C> &B, int64_t fstride,
+                                   const T (&acc)[N + 1][5], T *__restrict__ rhs)
+{
+    constexpr int NODES = Shape<N, C>::kNodes;
+    if (active && L.k == 2) {
+#pragma unroll
+        for (int a = 0; a < N + 1; ++a) {
+            const int s = L.nb + a * L.step;
+            const T mJ = lds[Shape<N, C>::kMinusInvJ * NODES + s];
+            const int64_t g = B.g0 + s;
+#pragma unroll
+            for (int f = 0; f < 5; ++f)
+                rhs[f * fstride + g] = (lds[f * NODES + s] + lds[(5 + f) * NODES + s] + acc[a][f]) * mJ;
         }
     }
 }
@@ -514,7 +545,11 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     // phases C, D
     write_partials<T, N, C>(lds, L, active, acc);
     __syncthreads();
-    store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
+    if constexpr (C::kFinalizeInLine) {
+        finish_line<T, N, C>(lds, L, active, B, fstride, acc, rhs);
+    } else {
+        store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
+    }
 }
 
 // Persistent variant: the grid holds only resident workgroups; each walks

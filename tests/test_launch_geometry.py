@@ -19,7 +19,7 @@ PARTIAL_VALUES = 15  # 3 directions x 5 fields
 
 
 def launch_table():
-    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major)} parsed from esdg_api.hip."""
+    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major, finish_in_line)} from esdg_api.hip."""
     text = open(API).read()
     rows = re.findall(r"struct Launch<(double|float), (\d+)>\s*\{\s*using C = LaunchCfg<([^>]*)>;", text)
     table = {}
@@ -28,7 +28,8 @@ def launch_table():
         epb, nt = int(parts[0]), int(parts[1])
         metric = parts[3] != "false" if len(parts) > 3 else True
         dirmajor = parts[5] == "true" if len(parts) > 5 else False
-        table[(dt, int(n))] = (epb, nt, metric, dirmajor)
+        fin = parts[6] == "true" if len(parts) > 6 else False
+        table[(dt, int(n))] = (epb, nt, metric, dirmajor, fin)
     return table
 
 
@@ -51,12 +52,14 @@ def test_staged_value_count_matches_kernel():
 @pytest.mark.parametrize("N", range(1, 9))
 @pytest.mark.parametrize("nelem", [1, 2, 5, 13])
 def test_indices_in_bounds(dtype, N, nelem):
-    EPB, NT, metric_in_lds, dirmajor = launch_table()[(dtype, N)]
+    EPB, NT, metric_in_lds, dirmajor, fin = launch_table()[(dtype, N)]
     Nq = N + 1
     Nq2, Np = Nq * Nq, Nq ** 3
     NODES = EPB * Np
     staged = NODE_VALUES if metric_in_lds else 10
-    lds_values = max(staged, PARTIAL_VALUES) * NODES
+    partials = 10 if fin else PARTIAL_VALUES
+    region = max(staged, partials)
+    lds_values = (region + (1 if fin else 0)) * NODES
     lines = 3 * EPB * Nq2
     assert lines <= NT
     node_iters = (NODES + NT - 1) // NT
@@ -77,8 +80,11 @@ def test_indices_in_bounds(dtype, N, nelem):
                 g = g0 + tt
                 assert 0 <= g and 4 * fstride + g < 5 * fstride and 9 * fstride + g < 10 * fstride
                 assert (staged - 1) * NODES + tt < lds_values
-                assert (10 + 4) * NODES + tt < lds_values
-                out_written[g] += 1
+                if fin:
+                    assert region * NODES + tt < lds_values          # staged -1/J
+                else:
+                    assert (10 + 4) * NODES + tt < lds_values    # phase D reads
+                    out_written[g] += 1
         # phase B / C: line threads
         for task in range(NT):
             if dirmajor:
@@ -108,7 +114,12 @@ def test_indices_in_bounds(dtype, N, nelem):
                 else:
                     assert (3 * k + 2) * fstride + g0 + s < 9 * fstride  # direct metric loads
                 assert 9 * NODES + s < lds_values
-                assert (k * 5 + 4) * NODES + s < lds_values         # partial writes
+                if fin and k == 2:
+                    assert region * NODES + s < lds_values and 9 * NODES + s < lds_values
+                    assert 4 * fstride + g0 + s < 5 * fstride        # direct store
+                    out_written[g0 + s] += 1
+                else:
+                    assert (k * 5 + 4) * NODES + s < (region if fin else lds_values // NODES) * NODES
                 written[k, g0 + s] += 1
                 for l in range(a + 1, Nq):
                     assert a * Nq + l < Nq2 and l * Nq + a < Nq2    # D reads
