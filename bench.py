@@ -109,22 +109,49 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
     return results[True], results[False], info, wl
 
 
-def profile_pass(steps: int) -> dict:
+def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
     """Short run for hardware-counter collection under rocprofv3: one plain
-    copy kernel of known size (512 MiB read, 512 MiB written: the calibration
-    of FETCH_SIZE / WRITE_SIZE), then `steps` launches of the headline kernel."""
+    copy kernel of known size (esdg_probe_copy_f64: 512 MiB read, 512 MiB
+    written, the calibration of FETCH_SIZE / WRITE_SIZE), then `steps`
+    launches of the headline kernel."""
     import torch
+
+    from entropy_stable_dg_amd import probe
 
     dev = torch.device("cuda:0")
     n = (512 << 20) // 8
     src = torch.ones(n, dtype=torch.float64, device=dev)
     dst = torch.empty_like(src)
-    torch.add(src, 0.0, out=dst)  # elementwise copy kernel: reads n*8 B, writes n*8 B
+    # plain copy kernel (libesdg_probe): reads n*8 B, writes n*8 B
+    if probe.esdg_probe_copy_f64(src.data_ptr(), dst.data_ptr(), n,
+                                 torch.cuda.current_stream(dev).cuda_stream) != 0:
+        raise RuntimeError("copy probe failed")
     torch.cuda.synchronize()
     del src, dst
-    cold, hot, info, _ = time_workload(HEADLINE, steps, 2, 512e6)
-    return {"profile_pass": True, "copy_bytes_each_way": n * 8, "us_per_step": cold * 1e6,
-            "bytes_per_launch": info["bytes"], "kernel_source_hash": kernel_source_hash()}
+    cold, hot, info, _ = time_workload(workload, steps, 2, 512e6)
+    return {"profile_pass": True, "workload": workload, "copy_bytes_each_way": n * 8,
+            "us_per_step": cold * 1e6, "bytes_per_launch": info["bytes"],
+            "flops_per_launch": info["flops"], "kernel_source_hash": kernel_source_hash()}
+
+
+def cpu_one_core(wl, seconds: float) -> dict:
+    """The oracle on one host thread over a bounded leading slice of the
+    workload's elements (element-local work, so DOF/s carries over)."""
+    import oracle
+
+    ne = max(1, min(wl.nelem, 256))
+    q, phi, geom = wl.q[:, :ne], wl.phi[:ne], wl.geom[:, :ne]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.volume_rhs(q, phi, geom, wl.D, wl.N, threads=1)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    value = ne * wl.Np * reps / dt
+    log(f"cpu oracle 1 thread: {reps} x {ne} elements in {dt:.1f} s -> {value:.3e} DOF/s")
+    return {"value": value, "unit": "DOF-updates/s", "cores": 1,
+            "sample": f"{reps} evaluations of the first {ne} elements of {wl.name}"}
 
 
 def cpu_baseline(wl, min_seconds: float):
@@ -157,8 +184,12 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 counter passes (copy calibration + kernel)")
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, high_order)")
     ap.add_argument("--extra", default="bubble_f32",
                     help="comma-separated extra workloads to time (reported under 'extra')")
+    ap.add_argument("--all", action="store_true",
+                    help="time every workload (tiny, baroclinic, bubble_f32, high_order) as extras")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -177,7 +208,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}; kernel source {kernel_source_hash()}")
     if args.profile_pass:
-        print(json.dumps(profile_pass(args.steps)), flush=True)
+        print(json.dumps(profile_pass(args.steps, args.workload)), flush=True)
         return 0
 
     t_cold, t_hot, info, wl = time_workload(HEADLINE, args.steps, args.warmup, args.rotate_mb * 1e6)
@@ -187,19 +218,31 @@ def main() -> int:
     traffic = measured_traffic(HEADLINE, info["dtype"])
 
     extra = {}
-    for name in [x for x in args.extra.split(",") if x]:
+    names = [x for x in args.extra.split(",") if x]
+    if args.all:
+        names = ["tiny", "baroclinic", "bubble_f32", "high_order"]
+    for name in names:
         c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6)
         extra[name] = {
             "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
             "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
+            "hbm_frac": inf["bytes"] / c / 1e9 / perfmodel.PEAK_HBM_GBS,
+            "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
+                                      if inf["dtype"] == "f64" else None),
         }
         if inf["dtype"] == "f32" and inf["N"] == info["N"] and inf["nelem"] == info["nelem"]:
             extra[name]["speedup_over_fp64"] = (inf["dof"] / c) / value
 
+    from entropy_stable_dg_amd import probe
+    stream_gbs = probe.stream81_bandwidth()
+    log(f"HBM stream probe (8 reads : 1 write, fp64): {stream_gbs:.0f} GB/s")
+
     cpu = None
+    cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu1 = cpu_one_core(wl, max(1.0, args.cpu_seconds / 3))
 
     out = {
         "metric": METRIC,
@@ -235,6 +278,9 @@ def main() -> int:
         "hot_ms_per_step": t_hot * 1e3,
         "hot_dof_per_s": info["dof"] / t_hot,
         "kernel_source_hash": kernel_source_hash(),
+        "hbm_stream81_gbs": stream_gbs,
+        "frac_of_measured_stream": achieved_gbs / stream_gbs,
+        "cpu_oracle_one_core": cpu1,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)

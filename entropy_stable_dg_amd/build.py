@@ -15,6 +15,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libesdg.so")
 SOURCES = [os.path.join(CSRC, "esdg_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"), os.path.join(INCLUDE, "esdg.h")]
+# HBM streaming probes (measurement only), a library of their own
+PROBE_LIB = os.path.join(HERE, "libesdg_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
@@ -29,20 +32,26 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into entropy_stable_dg_amd/libesdg.so."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-o", tmp] + SOURCES
+def _compile(sources, out, verbose):
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-o", tmp] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the HIP sources: libesdg.so (the volume term) and
+    libesdg_probe.so (HBM streaming probes)."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 def is_stale() -> bool:
     """True when the library is missing or older than one of its sources."""
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(PROBE_LIB):
         return True
     t = os.path.getmtime(LIB)
     return any(os.path.getmtime(p) > t for p in DEPENDS)

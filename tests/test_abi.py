@@ -7,16 +7,35 @@ import re
 
 import pytest
 
-from entropy_stable_dg_amd import esdg
+from entropy_stable_dg_amd import esdg, probe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "esdg.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "esdg_probe.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(esdg_\w+)\s*\(", text)))
+
+
+def test_probe_library_exports_its_header():
+    assert declared_functions(PROBE_HEADER) == sorted(probe.EXPORTS)
+    lib = probe.load()
+    out = os.popen(f"nm -D --defined-only {probe.PROBE_LIB_PATH}").read()
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in probe.EXPORTS:
+        assert hasattr(lib, name) and name in syms
+
+
+def test_probe_argument_errors():
+    # validation before any HIP call: no launch happens here
+    for fn in (probe.esdg_probe_stream81_f64, probe.esdg_probe_copy_f64):
+        assert fn(0x1000, 0x2000, -1, 0) == -3
+        assert fn(0, 0x2000, 10, 0) == -1
+        assert fn(0x1000, 0, 10, 0) == -1
+        assert fn(0, 0, 0, 0) == 0
 
 
 def test_header_declares_the_boundary():
