@@ -134,6 +134,63 @@ def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
             "flops_per_launch": info["flops"], "kernel_source_hash": kernel_source_hash()}
 
 
+def time_ablation(steps: int, warmup: int) -> dict:
+    """The optimisation ladder (libesdg_ablation, thread-per-node kernels, one
+    variant per cumulative step) and the production kernel, timed on the
+    pages' ladder configuration: N = 4, refinement level 6 (262,144
+    elements, 32,768,000 DOF), fp64, the bubble workload tiled 64 times."""
+    import torch
+
+    from entropy_stable_dg_amd import ablation, esdg, inputs
+
+    wl = inputs.make(HEADLINE)
+    dev = torch.device("cuda:0")
+    reps = 64
+    q, phi, geom, D = (torch.from_numpy(a).to(dev) for a in (wl.q, wl.phi, wl.geom, wl.D))
+    q, phi, geom = q.repeat(1, reps, 1), phi.repeat(reps, 1), geom.repeat(1, reps, 1)
+    rhs = torch.empty_like(q)
+    nelem, N = q.shape[1], wl.N
+    handle = torch.cuda.current_stream(dev).cuda_stream
+    args = (q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), N, nelem, rhs.data_ptr(), handle)
+
+    def timed(call) -> float:
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(f"ablation launch failed with status {st}")
+
+    ladder = []
+    for v in range(ablation.ESDG_ABL_COUNT):
+        ms = timed(lambda: check(ablation.esdg_ablation_volume_rhs_f64(v, *args)))
+        vf = v | ablation.ESDG_ABL_FUSE_FLAG
+        msf = timed(lambda: check(ablation.esdg_ablation_volume_rhs_f64(vf, *args)))
+        ladder.append({"variant": v, "name": ablation.esdg_ablation_name(v), "ms": ms,
+                       "ms_fused": msf})
+        log(f"ablation {v} ({ladder[-1]['name']}): {ms:.3f} ms; directions fused {msf:.3f} ms")
+    prod = timed(lambda: check(esdg.esdg_volume_rhs_f64(*args)))
+    log(f"ablation production kernel: {prod:.3f} ms")
+    base = ladder[0]["ms"]
+    for r in ladder:
+        r["speedup_vs_baseline"] = base / r["ms"]
+        r["speedup_fused_vs_baseline"] = base / r["ms_fused"]
+    dof = nelem * wl.Np
+    del q, phi, geom, rhs
+    torch.cuda.empty_cache()
+    return {"config": f"N={N}, {nelem} elements ({dof} DOF), fp64, bubble tiled {reps}x, hot buffers",
+            "steps": steps, "ladder": ladder,
+            "production": {"ms": prod, "speedup_vs_baseline": base / prod, "dof_per_s": dof / (prod * 1e-3)}}
+
+
 def cpu_one_core(wl, seconds: float) -> dict:
     """The oracle on one host thread over a bounded leading slice of the
     workload's elements (element-local work, so DOF/s carries over)."""
@@ -188,6 +245,9 @@ def main() -> int:
                     help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, high_order)")
     ap.add_argument("--extra", default="bubble_f32",
                     help="comma-separated extra workloads to time (reported under 'extra')")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
+    ap.add_argument("--ablation-steps", type=int, default=10)
     ap.add_argument("--all", action="store_true",
                     help="time every workload (tiny, baroclinic, bubble_f32, high_order) as extras")
     args = ap.parse_args()
@@ -233,6 +293,10 @@ def main() -> int:
         }
         if inf["dtype"] == "f32" and inf["N"] == info["N"] and inf["nelem"] == info["nelem"]:
             extra[name]["speedup_over_fp64"] = (inf["dof"] / c) / value
+
+    ablation = None
+    if not args.no_ablation:
+        ablation = time_ablation(args.ablation_steps, 2)
 
     from entropy_stable_dg_amd import probe
     stream_gbs = probe.stream81_bandwidth()
@@ -282,6 +346,7 @@ def main() -> int:
         "frac_of_measured_stream": achieved_gbs / stream_gbs,
         "cpu_oracle_one_core": cpu1,
         "extra": extra,
+        "ablation": ablation,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -1,4 +1,5 @@
-"""Build libesdg.so (HIP, gfx950) in-tree with hipcc.
+"""Build libesdg.so, libesdg_probe.so and libesdg_ablation.so (HIP, gfx950)
+in-tree with hipcc.
 
     python -m entropy_stable_dg_amd.build
 """
@@ -18,6 +19,11 @@ DEPENDS = SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"), os.path.join(INCLU
 # HBM streaming probes (measurement only), a library of their own
 PROBE_LIB = os.path.join(HERE, "libesdg_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
+# the optimisation-ladder variants of the volume term (measurement only)
+ABLATION_LIB = os.path.join(HERE, "libesdg_ablation.so")
+ABLATION_SOURCES = [os.path.join(CSRC, "ablation.hip")]
+ABLATION_DEPENDS = ABLATION_SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"),
+                                       os.path.join(INCLUDE, "esdg_ablation.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
@@ -43,18 +49,23 @@ def _compile(sources, out, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the HIP sources: libesdg.so (the volume term) and
-    libesdg_probe.so (HBM streaming probes)."""
+    """Compile the HIP sources: libesdg.so (the volume term),
+    libesdg_probe.so (HBM streaming probes) and libesdg_ablation.so (the
+    optimisation-ladder variants)."""
     _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    _compile(ABLATION_SOURCES, ABLATION_LIB, verbose)
     return _compile(SOURCES, LIB, verbose)
 
 
 def is_stale() -> bool:
     """True when the library is missing or older than one of its sources."""
-    if not os.path.exists(LIB) or not os.path.exists(PROBE_LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in DEPENDS)
+    for lib, deps in ((LIB, DEPENDS), (PROBE_LIB, PROBE_SOURCES), (ABLATION_LIB, ABLATION_DEPENDS)):
+        if not os.path.exists(lib):
+            return True
+        t = os.path.getmtime(lib)
+        if any(os.path.getmtime(p) > t for p in deps):
+            return True
+    return False
 
 
 if __name__ == "__main__":
