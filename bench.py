@@ -50,7 +50,8 @@ def measured_traffic(workload: str, dtype: str):
         return None
     with open(path) as f:
         data = json.load(f)
-    rec = data.get(f"{workload}_{dtype}")
+    base = workload[:-4] if workload.endswith("_f32") else workload
+    rec = data.get(f"{base}_{dtype}")
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
@@ -286,6 +287,7 @@ def main() -> int:
         extra[name] = {
             "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
+            "traffic": measured_traffic(name, inf["dtype"]),
             "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
             "hbm_frac": inf["bytes"] / c / 1e9 / perfmodel.PEAK_HBM_GBS,
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
@@ -299,8 +301,11 @@ def main() -> int:
         ablation = time_ablation(args.ablation_steps, 2)
 
     from entropy_stable_dg_amd import probe
-    stream_gbs = probe.stream81_bandwidth()
-    log(f"HBM stream probe (8 reads : 1 write, fp64): {stream_gbs:.0f} GB/s")
+    stream_narrow = probe.stream81_bandwidth()
+    stream_wide = probe.stream81_bandwidth(wide=True)
+    stream_gbs = max(stream_narrow, stream_wide)
+    log(f"HBM stream probe (8 reads : 1 write, fp64): {stream_narrow:.0f} GB/s with 8-byte lanes, "
+        f"{stream_wide:.0f} GB/s with 32-byte lanes")
 
     cpu = None
     cpu1 = None
@@ -343,6 +348,7 @@ def main() -> int:
         "hot_dof_per_s": info["dof"] / t_hot,
         "kernel_source_hash": kernel_source_hash(),
         "hbm_stream81_gbs": stream_gbs,
+        "hbm_stream81_gbs_by_lane_width": {"8B": stream_narrow, "32B": stream_wide},
         "frac_of_measured_stream": achieved_gbs / stream_gbs,
         "cpu_oracle_one_core": cpu1,
         "extra": extra,

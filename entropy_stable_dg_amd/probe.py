@@ -7,7 +7,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_LIB_PATH = os.path.join(HERE, "libesdg_probe.so")
-EXPORTS = ("esdg_probe_stream81_f64", "esdg_probe_copy_f64")
+EXPORTS = ("esdg_probe_stream81_f64", "esdg_probe_stream81_wide_f64", "esdg_probe_copy_f64")
 
 _lib = None
 
@@ -36,27 +36,33 @@ def esdg_probe_stream81_f64(src: int, dst: int, n: int, stream: int = 0) -> int:
     return load().esdg_probe_stream81_f64(src, dst, n, stream)
 
 
+def esdg_probe_stream81_wide_f64(src: int, dst: int, n: int, stream: int = 0) -> int:
+    return load().esdg_probe_stream81_wide_f64(src, dst, n, stream)
+
+
 def esdg_probe_copy_f64(src: int, dst: int, n: int, stream: int = 0) -> int:
     return load().esdg_probe_copy_f64(src, dst, n, stream)
 
 
-def stream81_bandwidth(n: int = 1 << 25, reps: int = 20) -> float:
+def stream81_bandwidth(n: int = 1 << 25, reps: int = 20, wide: bool = False) -> float:
     """Empirical HBM bandwidth (GB/s) of the 8-read:1-write fp64 stream on
-    cuda:0: 9 * 8 * n bytes per launch, reps back-to-back launches."""
+    cuda:0: 9 * 8 * n bytes per launch, reps back-to-back launches; `wide`
+    selects the 32-bytes-per-lane form."""
     import torch
 
     dev = torch.device("cuda:0")
     src = torch.ones(8 * n, dtype=torch.float64, device=dev)
     dst = torch.empty(n, dtype=torch.float64, device=dev)
     h = torch.cuda.current_stream(dev).cuda_stream
+    fn = esdg_probe_stream81_wide_f64 if wide else esdg_probe_stream81_f64
     for _ in range(3):
-        if esdg_probe_stream81_f64(src.data_ptr(), dst.data_ptr(), n, h) != 0:
+        if fn(src.data_ptr(), dst.data_ptr(), n, h) != 0:
             raise RuntimeError("stream probe launch failed")
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        esdg_probe_stream81_f64(src.data_ptr(), dst.data_ptr(), n, h)
+        fn(src.data_ptr(), dst.data_ptr(), n, h)
     t1.record()
     torch.cuda.synchronize()
     sec = t0.elapsed_time(t1) * 1e-3 / reps

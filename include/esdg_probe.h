@@ -12,7 +12,8 @@
  *
  * All pointers are device pointers owned by the caller; calls are
  * asynchronous on `stream`, allocate nothing and return a status:
- * 0 ok, -1 NULL pointer (n > 0), -3 n < 0 or too large, -4 launch failure.
+ * 0 ok, -1 NULL pointer (n > 0), -2 misaligned (wide form only), -3 n < 0
+ * or too large, -4 launch failure.
  * n == 0 is a no-op.
  */
 #ifndef ESDG_PROBE_H
@@ -27,6 +28,10 @@ extern "C" {
 
 /* dst[i] = sum_{j<8} src[j*n + i], i < n: reads 64 n bytes, writes 8 n bytes. */
 int esdg_probe_stream81_f64(const double *src, double *dst, int64_t n, hipStream_t stream);
+
+/* The same stream with 32 bytes per lane per array (16-byte loads); src and
+ * dst 16-byte aligned and n even, else -2. */
+int esdg_probe_stream81_wide_f64(const double *src, double *dst, int64_t n, hipStream_t stream);
 
 /* dst[i] = src[i], i < n: reads and writes 8 n bytes. */
 int esdg_probe_copy_f64(const double *src, double *dst, int64_t n, hipStream_t stream);

@@ -31,11 +31,16 @@ def test_probe_library_exports_its_header():
 
 def test_probe_argument_errors():
     # validation before any HIP call: no launch happens here
-    for fn in (probe.esdg_probe_stream81_f64, probe.esdg_probe_copy_f64):
+    for fn in (probe.esdg_probe_stream81_f64, probe.esdg_probe_stream81_wide_f64,
+               probe.esdg_probe_copy_f64):
         assert fn(0x1000, 0x2000, -1, 0) == -3
         assert fn(0, 0x2000, 10, 0) == -1
         assert fn(0x1000, 0, 10, 0) == -1
         assert fn(0, 0, 0, 0) == 0
+    # the wide form needs 16-byte alignment and an even length
+    assert probe.esdg_probe_stream81_wide_f64(0x1008, 0x2000, 10, 0) == -2
+    assert probe.esdg_probe_stream81_wide_f64(0x1000, 0x2008, 10, 0) == -2
+    assert probe.esdg_probe_stream81_wide_f64(0x1000, 0x2000, 11, 0) == -2
 
 
 def test_header_declares_the_boundary():

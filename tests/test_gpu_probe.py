@@ -8,7 +8,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n", [1, 2, 1000, 262145])
+@pytest.mark.parametrize("n", [1, 2, 6, 1000, 262145, 262146])
 def test_stream81_and_copy(n):
     assert torch.cuda.is_available()
     dev = torch.device("cuda:0")
@@ -23,6 +23,11 @@ def test_stream81_and_copy(n):
     for j in range(1, 8):
         expect += ref[j]          # same summation order as the kernel
     assert torch.equal(dst.cpu(), expect)
+    if n % 2 == 0:   # the 32-byte-lane form (even n, aligned arrays)
+        wide = torch.full((n,), -1.0, dtype=torch.float64, device=dev)
+        assert probe.esdg_probe_stream81_wide_f64(src.data_ptr(), wide.data_ptr(), n, h) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(wide.cpu(), expect)
     out = torch.empty(n, dtype=torch.float64, device=dev)
     assert probe.esdg_probe_copy_f64(src.data_ptr(), out.data_ptr(), n, h) == 0
     torch.cuda.synchronize()
@@ -32,4 +37,7 @@ def test_stream81_and_copy(n):
 def test_stream81_bandwidth_is_positive():
     bw = probe.stream81_bandwidth(n=1 << 22, reps=5)
     print(f"[probe] stream 8:1 fp64 at 4M doubles per array: {bw:.0f} GB/s", flush=True)
+    assert 100.0 < bw < 20000.0
+    bw = probe.stream81_bandwidth(n=1 << 22, reps=5, wide=True)
+    print(f"[probe] same, 32-byte lanes: {bw:.0f} GB/s", flush=True)
     assert 100.0 < bw < 20000.0
