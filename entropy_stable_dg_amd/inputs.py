@@ -250,6 +250,34 @@ def state_channel(X, L, T0=300.0, T_noise=1.0, u_max=35.0, rng=None):
 # ---------------------------------------------------------------------------
 # Named workloads
 # ---------------------------------------------------------------------------
+# Face order of the connectivity array: -xi1, +xi1, -xi2, +xi2, -xi3, +xi3.
+FACE_WALL = -1
+
+
+def box_connectivity(K, periodic=(True, True, True)) -> np.ndarray:
+    """Face neighbours nbr[nelem][6] (int32) of the box mesh of box_mesh():
+    element e = ex + Kx*(ey + Ky*ez); face 2k is the -xi_(k+1) face, 2k+1 the
+    +xi_(k+1) face; the neighbour across a face holds the matching nodes on
+    its opposite face with the same tangential indices.  Faces on the box
+    boundary wrap around where `periodic` says so, else are FACE_WALL."""
+    Kx, Ky, Kz = K
+    Ks = (Kx, Ky, Kz)
+    EZ, EY, EX = np.meshgrid(np.arange(Kz), np.arange(Ky), np.arange(Kx), indexing="ij")
+    idx = [EX.ravel(), EY.ravel(), EZ.ravel()]
+    nbr = np.empty((idx[0].size, 6), dtype=np.int32)
+    for k in range(3):
+        for side, step in ((0, -1), (1, 1)):
+            c = [i.copy() for i in idx]
+            c[k] = c[k] + step
+            out = (c[k] < 0) | (c[k] >= Ks[k])
+            c[k] = np.mod(c[k], Ks[k])
+            e = c[0] + Kx * (c[1] + Ky * c[2])
+            if not periodic[k]:
+                e = np.where(out, FACE_WALL, e)
+            nbr[:, 2 * k + side] = e
+    return nbr
+
+
 @dataclasses.dataclass
 class Workload:
     name: str
@@ -263,6 +291,8 @@ class Workload:
     seed: int
     dtype: str
     description: str
+    nbr: np.ndarray = None          # [nelem][6] face neighbours (FACE_WALL = slip wall)
+    periodic: tuple = (True, True, True)
 
     @property
     def Np(self) -> int:
@@ -275,7 +305,8 @@ class Workload:
 
 def build_workload(name: str, K, lo, hi, N: int, state: str, seed: int,
                    warp_frac: float = 0.0, dtype: str = "f64", description: str = "",
-                   warp_wavelength=None, state_kwargs=None) -> Workload:
+                   warp_wavelength=None, state_kwargs=None,
+                   periodic=(True, True, True)) -> Workload:
     """Mesh + metrics + state for an arbitrary box; the named configs below use it."""
     rng = np.random.default_rng(seed)
     D = diff_matrix(N)
@@ -302,30 +333,30 @@ def build_workload(name: str, K, lo, hi, N: int, state: str, seed: int,
     elif dtype != "f64":
         raise ValueError(dtype)
     return Workload(name, N, nelem, q, phi, np.ascontiguousarray(geom), np.ascontiguousarray(D),
-                    Xf, seed, dtype, description)
+                    Xf, seed, dtype, description, box_connectivity(K, periodic), tuple(periodic))
 
 
 # The five workloads: sizes and state recipes.
 CONFIGS = {
     "tiny": dict(K=(4, 4, 4), lo=(0, 0, 0), hi=(1, 1, 1), N=3, state="isothermal", seed=101,
-                 state_kwargs=dict(u_noise=1.0, rho_noise=1e-3),
+                 state_kwargs=dict(u_noise=1.0, rho_noise=1e-3), periodic=(True, True, False),
                  description="4x4x4 affine hexes on the unit cube, N=3, isothermal hydrostatic "
                              "(T0=300 K) + U(-1,1) m/s velocity and 1e-3 relative density noise"),
     "bubble": dict(K=(16, 16, 16), lo=(0, 0, 0), hi=(1000, 1000, 1000), N=4, state="bubble",
-                   seed=202,
+                   seed=202, periodic=(True, True, False),
                    description="16^3 affine hexes on [0,1000]^3 m, N=4, isentropic base "
                                "theta0=300 K + cosine bubble (0.5 K, r=250 m, centre "
                                "(500,500,350)) + U(-1e-3,1e-3) m/s velocity noise"),
     "baroclinic": dict(K=(80, 16, 8), lo=(0, 0, 0), hi=(4.0e7, 6.0e6, 3.0e4), N=4,
-                       state="channel", seed=303, warp_frac=0.05,
+                       state="channel", seed=303, warp_frac=0.05, periodic=(True, False, False),
                        description="80x16x8 hexes on a 40000x6000x30 km channel, N=4, "
                                    "isothermal 300 K base + U(-1,1) K noise, zonal jet 35 m/s, "
                                    "seeded sinusoidal warp of 5% of the element size"),
     "bubble_f32": dict(K=(16, 16, 16), lo=(0, 0, 0), hi=(1000, 1000, 1000), N=4, state="bubble",
-                       seed=202, dtype="f32",
+                       seed=202, dtype="f32", periodic=(True, True, False),
                        description="the rising-bubble workload rounded to fp32"),
     "high_order": dict(K=(24, 24, 24), lo=(0, 0, 0), hi=(1000, 1000, 1000), N=7, state="bubble",
-                       seed=505, warp_frac=0.05,
+                       seed=505, warp_frac=0.05, periodic=(True, True, False),
                        description="24^3 warped hexes on [0,1000]^3 m, N=7, rising-bubble "
                                    "state, 5% sinusoidal warp"),
 }

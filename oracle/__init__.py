@@ -65,6 +65,9 @@ class Oracle:
         lib.oracle_ec_flux.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int64, _P]
         lib.oracle_node_state.restype = None
         lib.oracle_node_state.argtypes = [_P, _P, ctypes.c_int64, _P]
+        lib.oracle_surface_rhs.restype = ctypes.c_int
+        lib.oracle_surface_rhs.argtypes = [_P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                           ctypes.c_int64, _P, _P, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         self.lib = lib
@@ -92,6 +95,41 @@ class Oracle:
                                         int(threads))
         if rc != 0:
             raise ValueError(f"oracle_volume_rhs failed ({rc})")
+        return (rhs, mag) if with_magnitude else rhs
+
+    def surface_rhs(self, q, phi, geom, nbr, N: int, *, rhs=None, mag=None, threads: int = 0):
+        """Surface term of the semi-discrete ESDG form with the entropy-
+        conservative flux, added to ``rhs`` (zeros when None) and returned;
+        ``mag`` (optional) accumulates its absolute values.  nbr [nelem][6]
+        int32 face neighbours, -1 = slip wall."""
+        q, phi, geom = _f64(q), _f64(phi), _f64(geom)
+        nbr = np.ascontiguousarray(nbr, dtype=np.int32)
+        Np = (N + 1) ** 3
+        nelem = phi.size // Np
+        if q.size != 5 * nelem * Np or geom.size != 10 * nelem * Np or nbr.shape != (nelem, 6):
+            raise ValueError("array sizes do not match N and nelem")
+        if rhs is None:
+            rhs = np.zeros((5, nelem, Np))
+        if rhs.dtype != np.float64 or not rhs.flags.c_contiguous or rhs.size != 5 * nelem * Np:
+            raise ValueError("rhs must be a contiguous float64 [5][nelem][Np] array")
+        if mag is not None and (mag.dtype != np.float64 or not mag.flags.c_contiguous
+                                or mag.size != 5 * nelem * Np):
+            raise ValueError("mag must be a contiguous float64 [5][nelem][Np] array")
+        rc = self.lib.oracle_surface_rhs(_ptr(q), _ptr(phi), _ptr(geom),
+                                         nbr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, nelem,
+                                         _ptr(rhs), _ptr(mag) if mag is not None else None,
+                                         int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle_surface_rhs failed ({rc})")
+        return rhs
+
+    def rhs(self, q, phi, geom, D, nbr, N: int, *, with_magnitude: bool = False,
+            threads: int = 0):
+        """Whole semi-discrete right-hand side (volume + entropy-conservative
+        surface term, h = 0)."""
+        out = self.volume_rhs(q, phi, geom, D, N, with_magnitude=with_magnitude, threads=threads)
+        rhs, mag = out if with_magnitude else (out, None)
+        self.surface_rhs(q, phi, geom, nbr, N, rhs=rhs, mag=mag, threads=threads)
         return (rhs, mag) if with_magnitude else rhs
 
     def ec_flux(self, qi, phii, ql, phil, j: int) -> np.ndarray:
@@ -135,6 +173,14 @@ def volume_rhs(*args, **kwargs):
 
 def ec_flux(*args, **kwargs):
     return default().ec_flux(*args, **kwargs)
+
+
+def surface_rhs(*args, **kwargs):
+    return default().surface_rhs(*args, **kwargs)
+
+
+def rhs(*args, **kwargs):
+    return default().rhs(*args, **kwargs)
 
 
 def node_state(*args, **kwargs):

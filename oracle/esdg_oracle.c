@@ -16,6 +16,9 @@
  *   mean / log mean / jump ............... [ESDG-GPU §4.1, Eq. 3]
  *   momentum flux with gravity ........... [ESDG-GPU §4.1, Eq. 4 and Eq. 5]
  *   diagonal pairs omitted ............... [ESDG-GPU §4.1, Fig. 1 caption]
+ *   surface term ......................... [ESDG-GPU §3, Eq. 2 (second brace) and the text
+ *                                           after it: minus side = own element, plus side =
+ *                                           the neighbour]
  *
  * Readings of the pages that this file takes (the pages print the momentum
  * component only; the other components are fixed by entropy conservation,
@@ -32,6 +35,22 @@
  *                          sum_j (Ja^k_j(i) + Ja^k_j(l)) F_j(q_i, q_l)
  *     (l runs over the nodes of the k-line through i); the source h is zero;
  *   - gamma = 1.4.
+ *
+ * Readings for the surface term (oracle_surface_rhs):
+ *   - F* is the same two-point flux as in the volume (entropy conservative,
+ *     with its gravity term); the matrix dissipation the pages add to it is
+ *     not printed on the pages and is left out;
+ *   - M^{-1} M^s G^s_jk F*_j at a node i on the xi_k = +-1 face of an element
+ *     is (+-1) Ja^k_j(i) F*_j / (w_end J_i): the surface quadrature weights
+ *     cancel against the tangential part of the tensor-product volume
+ *     weights, leaving the 1D LGL end weight w_end = 2/(N(N+1)), and the
+ *     area-weighted outward normal is +-Ja^k at that face;
+ *   - neighbours share the face node for node (conforming, same orientation):
+ *     the partner of node (.., i_k = N, ..) across the +xi_k face is node
+ *     (.., i_k = 0, ..) of the neighbour, and the other way round;
+ *   - a slip wall takes as partner the mirror state of the own node: the same
+ *     density, pressure and geopotential, velocity reflected in the face
+ *     normal Ja^k(i).
  *
  * Every ordered pair is evaluated on its own: no symmetry, no hoisting, no
  * reuse.  That is the plain definition of what the volume term computes.
@@ -216,6 +235,82 @@ int oracle_volume_rhs(const double *q, const double *phi, const double *geom,
             }
         }
         free(st);
+    }
+    return 0;
+}
+
+/*
+ * Surface term of Eq. 2 with the entropy-conservative flux (readings above),
+ * ADDED to rhs (and, if mag is not NULL, its absolute value to mag).
+ *
+ *   nbr [nelem][6]  neighbour across faces -xi1, +xi1, -xi2, +xi2, -xi3,
+ *                   +xi3; -1 = slip wall
+ *
+ * Returns 0, -1 on bad sizes, -2 if a neighbour index is outside [-1, nelem).
+ */
+int oracle_surface_rhs(const double *q, const double *phi, const double *geom,
+                       const int32_t *nbr, int N, int64_t nelem, double *rhs, double *mag,
+                       int nthreads)
+{
+    if (N < 1 || nelem < 0) return -1;
+    for (int64_t i = 0; i < 6 * nelem; ++i)
+        if (nbr[i] < -1 || nbr[i] >= nelem) return -2;
+    const int Nq = N + 1;
+    const int64_t Np = (int64_t)Nq * Nq * Nq;
+    const int64_t stride = nelem * Np;
+    const double w_end = 2.0 / ((double)N * (double)(N + 1));  /* LGL weight of xi = +-1 */
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+#else
+    (void)nthreads;
+#endif
+    for (int64_t e = 0; e < nelem; ++e) {
+        for (int c = 0; c < Nq; ++c)
+        for (int b = 0; b < Nq; ++b)
+        for (int a = 0; a < Nq; ++a) {
+            const int64_t i = a + Nq * (b + Nq * c);
+            double qi[5];
+            for (int f = 0; f < 5; ++f) qi[f] = q[f * stride + e * Np + i];
+            const node_state si = read_node(qi, phi[e * Np + i]);
+            const double Ji = geom[9 * stride + e * Np + i];
+            for (int k = 0; k < 3; ++k) {
+                const int ik = (k == 0) ? a : (k == 1) ? b : c;
+                if (ik != 0 && ik != N) continue;  /* not on a xi_k face */
+                const int side = (ik == N) ? 1 : -1;
+                const int32_t nb = nbr[6 * e + 2 * k + (side > 0 ? 1 : 0)];
+                double n[3];
+                for (int j = 0; j < 3; ++j) n[j] = geom[(3 * k + j) * stride + e * Np + i];
+                node_state sp;
+                if (nb < 0) {
+                    /* mirror state across the face */
+                    sp = si;
+                    const double un = (si.u[0] * n[0] + si.u[1] * n[1] + si.u[2] * n[2])
+                                    / (n[0] * n[0] + n[1] * n[1] + n[2] * n[2]);
+                    for (int j = 0; j < 3; ++j) sp.u[j] = si.u[j] - 2.0 * un * n[j];
+                    sp.usq = sp.u[0] * sp.u[0] + sp.u[1] * sp.u[1] + sp.u[2] * sp.u[2];
+                } else {
+                    const int jk = N - ik;  /* matching node on the neighbour's opposite face */
+                    const int64_t ip = (k == 0) ? jk + Nq * (b + Nq * c)
+                                     : (k == 1) ? a + Nq * (jk + Nq * c)
+                                                : a + Nq * (b + Nq * jk);
+                    double qp[5];
+                    for (int f = 0; f < 5; ++f) qp[f] = q[f * stride + (int64_t)nb * Np + ip];
+                    sp = read_node(qp, phi[(int64_t)nb * Np + ip]);
+                }
+                double term[5] = {0, 0, 0, 0, 0};
+                for (int j = 0; j < 3; ++j) {
+                    double F[5];
+                    ec_flux(&si, &sp, j, F);
+                    for (int f = 0; f < 5; ++f) term[f] += n[j] * F[f];
+                }
+                for (int f = 0; f < 5; ++f) {
+                    const double v = (double)side * term[f] / (w_end * Ji);
+                    rhs[f * stride + e * Np + i] -= v;
+                    if (mag) mag[f * stride + e * Np + i] += fabs(v);
+                }
+            }
+        }
     }
     return 0;
 }

@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as P
+from tests import test_oracle_surface as S
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "esdg_oracle.c")
 
@@ -44,6 +45,20 @@ MUTANTS = [
      ": (k == 1) ? a + Nq * (l + Nq * c)", ": (k == 1) ? l + Nq * (b + Nq * c)"),
     ("energy flux with the full momentum flux (gravity included)",
      "if (m == j) sym += p_tilde;", "if (m == j) sym += p_tilde + 0.5 * rho_hat * phi_jump;"),
+    # surface term
+    ("surface term with the wrong face sign",
+     "const int side = (ik == N) ? 1 : -1;", "const int side = (ik == N) ? -1 : 1;"),
+    ("surface weight 1/(N(N+1)) instead of the LGL end weight",
+     "const double w_end = 2.0 / ((double)N * (double)(N + 1));",
+     "const double w_end = 1.0 / ((double)N * (double)(N + 1));"),
+    ("neighbour's node not taken on the opposite face",
+     "const int jk = N - ik;", "const int jk = ik;"),
+    ("wall partner not reflected",
+     "sp.u[j] = si.u[j] - 2.0 * un * n[j];", "sp.u[j] = si.u[j];"),
+    ("wall reflection with an unnormalised normal",
+     "/ (n[0] * n[0] + n[1] * n[1] + n[2] * n[2]);", ";"),
+    ("surface term without 1/J",
+     "(double)side * term[f] / (w_end * Ji);", "(double)side * term[f] / w_end;"),
 ]
 
 # a cheap battery of pins: every check raises AssertionError on a mismatch
@@ -56,6 +71,12 @@ BATTERY = [
     (P.check_isothermal_hydrostatic, (3, False)), (P.check_isothermal_hydrostatic, (4, True)),
     (P.check_cartesian_reduction, (1,)),
     (P.check_element_vs_50_digits, (1,)),
+    (S.check_global_entropy_conservation, (2, (True, True, True))),
+    (S.check_global_entropy_conservation, (3, (True, False, False))),
+    (S.check_conservation, (3, (True, False, False))),
+    (S.check_free_stream_full, (2, (True, True, True))),
+    (S.check_hydrostatic_full, (3, 0.05)),
+    (S.check_surface_vs_50_digits, (1,)),
 ]
 
 

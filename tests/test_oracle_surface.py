@@ -1,0 +1,281 @@
+"""Pins of the oracle's surface term (entropy-conservative face flux, periodic
+and slip-wall faces) and of the whole semi-discrete right-hand side it forms
+with the volume term.
+
+Page: "GPU Performance of an Entropy-Stable Discontinuous Galerkin Euler
+Solver with Non-Conservative Terms" (arXiv 2605.16684v2), [ESDG-GPU] §3, Eq. 2.
+
+  global entropy conservation ........ the volume and surface fluxes are both
+                                       entropy conservative ([ESDG-GPU §3]):
+                                       sum_e sum_i w_i J_i v_i . rhs_i = 0 on a
+                                       closed mesh (periodic faces, slip walls)
+  conservation of mass and energy .... sum w J rhs^rho = sum w J rhs^E = 0;
+                                       momentum too when phi is constant and
+                                       every face is periodic
+  free stream, curved mesh ........... constant state, constant phi: rhs = 0
+                                       (the volume term's face residual and the
+                                       surface term cancel; derived)
+  hydrostatic balance ................ isothermal atmosphere at rest between slip
+                                       walls: rhs = 0 (derived: the well-balanced
+                                       property of the non-conservative flux)
+  50-digit brute force ............... independent arbitrary-precision evaluation
+                                       of the surface term on a small mesh
+
+Entropy variables (derived, not on the pages): v = d eta / dq for
+eta = -rho s/(gamma-1), s = ln p - gamma ln rho, p = (gamma-1)(E - |m|^2/(2rho)
+- rho phi).
+"""
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import inputs as I
+from tests.test_oracle_pins import cons, entropy_vars, mp_flux, random_prims, weights3
+
+
+def periodic_mesh(K, N, warp, seed, periodic):
+    D = I.diff_matrix(N)
+    hi = tuple(1000.0 * k for k in K)
+    X = I.box_mesh(K, (0, 0, 0), hi, N, warp_frac=warp, seed=seed)
+    geom = I.metrics(X, D)
+    nbr = I.box_connectivity(K, periodic)
+    return D, X.reshape(3, X.shape[1], -1), geom, nbr
+
+
+def nodewise_random_state(rng, shape, phi_scale=1.0e4):
+    """Independent random state at every node (discontinuous across faces)."""
+    n = int(np.prod(shape))
+    rho, u, p, phi = random_prims(rng, n, phi_range=(0.0, phi_scale))
+    return rho.reshape(shape), u.reshape((3,) + shape), p.reshape(shape), phi.reshape(shape)
+
+
+def global_entropy_rate(rhs, geom, W, rho, u, p, phi):
+    """sum_e sum_i w_i J_i v_i . rhs_i and the sum of the absolute summands."""
+    ne = rho.shape[0]
+    total, scale = 0.0, 0.0
+    for e in range(ne):
+        v = entropy_vars(rho[e], u[:, e], p[e], phi[e])  # [Np][5]
+        terms = W[:, None] * geom[9, e][:, None] * v * rhs[:, e, :].T
+        total += terms.sum()
+        scale += np.abs(terms).sum()
+    return total, scale
+
+
+def check_global_entropy_conservation(orc, N, periodic, warp=0.05, seed=0):
+    rng = np.random.default_rng(200 + 10 * N + seed)
+    K = (3, 2, 2)
+    D, X, geom, nbr = periodic_mesh(K, N, warp, seed, periodic)
+    rho, u, p, phi = nodewise_random_state(rng, X[0].shape)
+    q = I.conserved(rho, u, p, phi)
+    rhs = orc.rhs(q, phi, geom, D, nbr, N)
+    W, _ = weights3(N)
+    total, scale = global_entropy_rate(rhs, geom, W, rho, u, p, phi)
+    assert abs(total) <= 1e-12 * scale, (total, scale)
+
+
+@pytest.mark.parametrize("N,periodic", [(1, (True, True, True)), (2, (True, True, True)),
+                                        (3, (True, False, True)), (4, (False, False, False)),
+                                        (7, (True, True, False))])
+def test_global_entropy_conservation(N, periodic):
+    check_global_entropy_conservation(oracle.default(), N, periodic)
+
+
+def test_surface_term_is_what_makes_entropy_vanish():
+    """The volume term alone does not conserve entropy globally on the same
+    mesh: the surface term carries the face contributions that cancel it."""
+    N, K = 3, (3, 2, 2)
+    rng = np.random.default_rng(5)
+    D, X, geom, nbr = periodic_mesh(K, N, 0.05, 1, (True, True, True))
+    rho, u, p, phi = nodewise_random_state(rng, X[0].shape)
+    q = I.conserved(rho, u, p, phi)
+    W, _ = weights3(N)
+    vol = oracle.volume_rhs(q, phi, geom, D, N)
+    total, scale = global_entropy_rate(vol, geom, W, rho, u, p, phi)
+    assert abs(total) > 1e-6 * scale
+
+
+def check_conservation(orc, N, periodic, const_phi=False):
+    rng = np.random.default_rng(300 + N)
+    K = (2, 3, 2)
+    D, X, geom, nbr = periodic_mesh(K, N, 0.05, 2, periodic)
+    rho, u, p, phi = nodewise_random_state(rng, X[0].shape)
+    if const_phi:
+        phi = np.full_like(phi, 123.0)
+    q = I.conserved(rho, u, p, phi)
+    rhs, mag = orc.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    W, _ = weights3(N)
+    wj = W[None, :] * geom[9]
+    fields = [0, 4] + ([1, 2, 3] if const_phi and all(periodic) else [])
+    for f in fields:
+        total = (wj * rhs[f]).sum()
+        scale = (wj * mag[f]).sum()
+        assert abs(total) <= 1e-12 * scale, (f, total, scale)
+
+
+@pytest.mark.parametrize("N,periodic,const_phi", [(2, (True, True, True), False),
+                                                  (3, (True, False, False), False),
+                                                  (4, (True, True, True), True),
+                                                  (2, (False, True, False), True)])
+def test_conservation(N, periodic, const_phi):
+    check_conservation(oracle.default(), N, periodic, const_phi)
+
+
+def check_free_stream_full(orc, N, periodic):
+    """Constant state on a curved mesh: rhs = 0.  With slip walls the state is
+    at rest (a moving constant state is not a solution there)."""
+    K = (2, 2, 2)
+    D, X, geom, nbr = periodic_mesh(K, N, 0.05, 3, periodic)
+    shape = X[0].shape
+    rho = np.full(shape, 1.1)
+    p = np.full(shape, 0.9e5)
+    phi = np.full(shape, 50.0)
+    u = np.zeros((3,) + shape)
+    if all(periodic):
+        u[0], u[1], u[2] = 30.0, -20.0, 10.0
+    q = I.conserved(rho, u, p, phi)
+    rhs, mag = orc.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    for f in range(5):
+        assert np.abs(rhs[f]).max() <= 1e-13 * max(np.abs(mag[f]).max(), 1e-300), f
+
+
+@pytest.mark.parametrize("N,periodic", [(2, (True, True, True)), (4, (True, True, True)),
+                                        (3, (True, False, False)), (7, (True, True, True))])
+def test_free_stream_full(N, periodic):
+    check_free_stream_full(oracle.default(), N, periodic)
+
+
+def check_hydrostatic_full(orc, N, warp):
+    """Isothermal atmosphere at rest (T0 = 300 K, phi = g z, p = p0 exp(-phi/(R T0)))
+    between slip walls at the bottom and top, periodic sideways: every
+    component of rhs vanishes to round-off, on affine and curved meshes."""
+    K = (2, 2, 3)
+    N_ = N
+    D = I.diff_matrix(N_)
+    X = I.box_mesh(K, (0, 0, 0), (2000, 2000, 3000), N_, warp_frac=warp, seed=4)
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    z = X.reshape(3, ne, -1)[2]
+    T0 = 300.0
+    phi = I.GRAV * z
+    p = I.P0 * np.exp(-phi / (I.R_GAS * T0))
+    rho = p / (I.R_GAS * T0)
+    u = np.zeros((3,) + rho.shape)
+    q = I.conserved(rho, u, p, phi)
+    nbr = I.box_connectivity(K, (True, True, False))
+    rhs, mag = orc.rhs(q, phi, geom, D, nbr, N_, with_magnitude=True)
+    for f in range(5):
+        assert np.abs(rhs[f]).max() <= 1e-14 * max(np.abs(mag[f]).max(), 1e-300), f
+
+
+@pytest.mark.parametrize("N,warp", [(2, 0.0), (3, 0.05), (4, 0.0), (4, 0.05), (7, 0.05)])
+def test_hydrostatic_full(N, warp):
+    check_hydrostatic_full(oracle.default(), N, warp)
+
+
+# --- 50-digit brute force of the surface term -------------------------------
+def mp_partner(q, phi, geom, nbr, N, e, abc, k):
+    """Conserved state and geopotential of the face partner of node abc of
+    element e across its xi_k face, at 50 digits."""
+    Nq = N + 1
+    a, b, c = abc
+    i = a + Nq * (b + Nq * c)
+    ik = abc[k]
+    nb = nbr[e, 2 * k + (1 if ik == N else 0)]
+    if nb >= 0:
+        jk = N - ik
+        ip = [jk + Nq * (b + Nq * c), a + Nq * (jk + Nq * c), a + Nq * (b + Nq * jk)][k]
+        return [mpmath.mpf(x) for x in q[:, nb, ip]], phi[nb, ip]
+    # slip wall: mirror state (same rho, p, phi; velocity reflected in Ja^k(i))
+    n = [mpmath.mpf(geom[3 * k + j, e, i]) for j in range(3)]
+    qq = [mpmath.mpf(x) for x in q[:, e, i]]
+    u = [qq[1 + m] / qq[0] for m in range(3)]
+    un = sum(u[m] * n[m] for m in range(3)) / sum(x * x for x in n)
+    um = [u[m] - 2 * un * n[m] for m in range(3)]
+    kin = qq[0] * sum(x * x for x in u) / 2
+    kin_m = qq[0] * sum(x * x for x in um) / 2
+    return [qq[0]] + [qq[0] * um[m] for m in range(3)] + [qq[4] - kin + kin_m], phi[e, i]
+
+
+def mp_surface_rhs(q, phi, geom, nbr, N):
+    """Surface term at 50 digits from its definition: a node on the
+    xi_k = +-1 face receives -(+-1) Ja^k(i) . F*(q_i, q_partner) / (w_end J_i)."""
+    Nq = N + 1
+    ne = nbr.shape[0]
+    w_end = mpmath.mpf(2) / (N * (N + 1))
+    out = np.zeros((5, ne, Nq ** 3))
+    for e in range(ne):
+        for c in range(Nq):
+            for b in range(Nq):
+                for a in range(Nq):
+                    i = a + Nq * (b + Nq * c)
+                    acc = [mpmath.mpf(0)] * 5
+                    for k in range(3):
+                        ik = (a, b, c)[k]
+                        if ik not in (0, N):
+                            continue
+                        side = 1 if ik == N else -1
+                        qp, php = mp_partner(q, phi, geom, nbr, N, e, (a, b, c), k)
+                        for j in range(3):
+                            nj = mpmath.mpf(geom[3 * k + j, e, i])
+                            F = mp_flux(q[:, e, i], phi[e, i], qp, php, j)
+                            for f in range(5):
+                                acc[f] += side * nj * F[f]
+                    J = mpmath.mpf(geom[9, e, i])
+                    for f in range(5):
+                        out[f, e, i] = float(-acc[f] / (w_end * J))
+    return out
+
+
+def check_surface_vs_50_digits(orc, N):
+    """A 2 x 1 x 1 mesh, periodic in x (each element's x-neighbour is the
+    other one), slip walls in y and z, random state and random metrics."""
+    rng = np.random.default_rng(400 + N)
+    K = (2, 1, 1)
+    Np = (N + 1) ** 3
+    ne = 2
+    rho, u, p, phi = nodewise_random_state(rng, (ne, Np))
+    q = I.conserved(rho, u, p, phi)
+    geom = rng.uniform(-1.0, 1.0, (10, ne, Np))
+    geom[9] = rng.uniform(0.5, 2.0, (ne, Np))
+    nbr = I.box_connectivity(K, (True, False, False))
+    ref = mp_surface_rhs(q, phi, geom, nbr, N)
+    got = orc.surface_rhs(q, phi, geom, nbr, N)
+    for f in range(5):
+        assert np.abs(got[f] - ref[f]).max() <= 1e-13 * np.abs(ref[f]).max(), f
+
+
+@pytest.mark.parametrize("N", [1, 2])
+def test_surface_vs_50_digits(N):
+    check_surface_vs_50_digits(oracle.default(), N)
+
+
+def test_surface_rejects_bad_neighbours():
+    N = 1
+    Np = 8
+    q = np.ones((5, 1, Np))
+    q[4] = 3e5
+    with pytest.raises(ValueError):
+        oracle.surface_rhs(q, np.zeros((1, Np)), np.ones((10, 1, Np)),
+                           np.array([[0, 0, 0, 0, 0, 1]], dtype=np.int32), N)
+    with pytest.raises(ValueError):
+        oracle.surface_rhs(q, np.zeros((1, Np)), np.ones((10, 1, Np)),
+                           np.array([[0, 0, 0, -2, 0, 0]], dtype=np.int32), N)
+
+
+def test_connectivity_of_the_box():
+    """box_connectivity: each periodic face pairs with the neighbour's opposite
+    face (nbr[nbr[e][2k+s]][2k+1-s] == e), walls only on non-periodic sides."""
+    K = (3, 2, 4)
+    for periodic in ((True, True, True), (True, False, True), (False, False, False)):
+        nbr = I.box_connectivity(K, periodic)
+        for e in range(nbr.shape[0]):
+            for f in range(6):
+                nb = nbr[e, f]
+                if nb == I.FACE_WALL:
+                    assert not periodic[f // 2]
+                else:
+                    assert nbr[nb, f ^ 1] == e
+        walls = (nbr == I.FACE_WALL).sum()
+        expect = sum(0 if periodic[k] else 2 * int(np.prod(K)) // K[k] for k in range(3))
+        assert walls == expect
