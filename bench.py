@@ -50,15 +50,16 @@ def measured_traffic(workload: str, dtype: str):
         return None
     with open(path) as f:
         data = json.load(f)
-    base = workload[:-4] if workload.endswith("_f32") else workload
+    base = workload.replace("_f32", "")
     rec = data.get(f"{base}_{dtype}")
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
 
-def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
-    """Returns (seconds per step rotating cold buffers, seconds per step hot, info)."""
+def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False):
+    """Returns (seconds per step rotating cold buffers, seconds per step hot, info).
+    With `full`, the whole right-hand side (volume + surface, esdg_rhs_*)."""
     import torch
 
     from entropy_stable_dg_amd import esdg, inputs, perfmodel
@@ -68,25 +69,31 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
     dev = torch.device("cuda:0")
     footprint = sum(a.nbytes for a in (wl.q, wl.phi, wl.geom)) + wl.q.nbytes
     nsets = max(2, math.ceil(rotate_bytes / footprint))
-    log(f"{name}: N={wl.N} nelem={wl.nelem} dof={wl.dof} dtype={dtype} "
-        f"footprint={footprint / 1e6:.1f} MB x {nsets} buffer sets")
-    host = [torch.from_numpy(a) for a in (wl.q, wl.phi, wl.geom, wl.D)]
+    log(f"{name}{' (whole rhs)' if full else ''}: N={wl.N} nelem={wl.nelem} dof={wl.dof} "
+        f"dtype={dtype} footprint={footprint / 1e6:.1f} MB x {nsets} buffer sets")
+    host = [torch.from_numpy(a) for a in (wl.q, wl.phi, wl.geom, wl.D, wl.nbr)]
     sets = []
     for _ in range(nsets):
-        q, phi, geom, D = (t.to(dev) for t in host)
+        q, phi, geom, D, nbr = (t.to(dev) for t in host)
         rhs = torch.empty_like(q)
-        sets.append((q, phi, geom, D, rhs))
-    fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
+        sets.append((q, phi, geom, D, nbr, rhs))
+    if full:
+        fn = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
+    else:
+        fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
-    ptrs = [(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), rhs.data_ptr())
-            for q, phi, geom, D, rhs in sets]
+    ptrs = [(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), nbr.data_ptr(),
+             rhs.data_ptr()) for q, phi, geom, D, nbr, rhs in sets]
     N, nelem = wl.N, wl.nelem
 
     def run(k: int, rotate: bool) -> None:
         for i in range(k):
             p = ptrs[i % nsets] if rotate else ptrs[0]
-            st = fn(p[0], p[1], p[2], p[3], N, nelem, p[4], handle)
+            if full:
+                st = fn(p[0], p[1], p[2], p[3], p[4], N, nelem, p[5], handle)
+            else:
+                st = fn(p[0], p[1], p[2], p[3], N, nelem, p[5], handle)
             if st != 0:
                 raise RuntimeError(esdg.esdg_status_string(st))
 
@@ -105,6 +112,10 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float):
                 seed=wl.seed, buffer_sets=nsets,
                 bytes=perfmodel.algorithmic_bytes(N, nelem, dtype),
                 flops=perfmodel.flops_per_element(N) * nelem)
+    if full:
+        info["bytes"] = perfmodel.algorithmic_bytes_rhs(N, nelem, dtype)
+        info["bytes_with_face_partners"] = info["bytes"] + perfmodel.face_partner_bytes(N, wl.nbr, dtype)
+        info["flops"] += perfmodel.surface_flops(N, wl.nbr)
     del sets
     torch.cuda.empty_cache()
     return results[True], results[False], info, wl
@@ -129,7 +140,8 @@ def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
         raise RuntimeError("copy probe failed")
     torch.cuda.synchronize()
     del src, dst
-    cold, hot, info, _ = time_workload(workload, steps, 2, 512e6)
+    name, _, mode = workload.partition(":")
+    cold, hot, info, _ = time_workload(name, steps, 2, 512e6, full=(mode == "rhs"))
     return {"profile_pass": True, "workload": workload, "copy_bytes_each_way": n * 8,
             "us_per_step": cold * 1e6, "bytes_per_launch": info["bytes"],
             "flops_per_launch": info["flops"], "kernel_source_hash": kernel_source_hash()}
@@ -243,9 +255,11 @@ def main() -> int:
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 counter passes (copy calibration + kernel)")
     ap.add_argument("--workload", default=HEADLINE,
-                    help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, high_order)")
-    ap.add_argument("--extra", default="bubble_f32",
-                    help="comma-separated extra workloads to time (reported under 'extra')")
+                    help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, "
+                         "high_order; a ':rhs' suffix profiles the whole right-hand side)")
+    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs",
+                    help="comma-separated extra workloads to time (reported under 'extra'); "
+                         "a ':rhs' suffix times the whole right-hand side (volume + surface)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
     ap.add_argument("--ablation-steps", type=int, default=10)
@@ -281,20 +295,27 @@ def main() -> int:
     extra = {}
     names = [x for x in args.extra.split(",") if x]
     if args.all:
-        names = ["tiny", "baroclinic", "bubble_f32", "high_order"]
-    for name in names:
-        c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6)
-        extra[name] = {
+        names = ["tiny", "baroclinic", "bubble_f32", "high_order", "bubble:rhs", "bubble_f32:rhs",
+                 "baroclinic:rhs", "high_order:rhs"]
+    for key in names:
+        name, _, mode = key.partition(":")
+        full = mode == "rhs"
+        c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6, full=full)
+        extra[key] = {
             "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
-            "traffic": measured_traffic(name, inf["dtype"]),
+            "traffic": measured_traffic(key.replace(":", "_"), inf["dtype"]),
             "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
             "hbm_frac": inf["bytes"] / c / 1e9 / perfmodel.PEAK_HBM_GBS,
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                       if inf["dtype"] == "f64" else None),
         }
-        if inf["dtype"] == "f32" and inf["N"] == info["N"] and inf["nelem"] == info["nelem"]:
-            extra[name]["speedup_over_fp64"] = (inf["dof"] / c) / value
+        if full:
+            extra[key]["hbm_gbs_with_face_partners"] = inf["bytes_with_face_partners"] / c / 1e9
+            extra[key]["what"] = "whole right-hand side: volume + entropy-conservative surface term"
+        if (inf["dtype"] == "f32" and not full and inf["N"] == info["N"]
+                and inf["nelem"] == info["nelem"]):
+            extra[key]["speedup_over_fp64"] = (inf["dof"] / c) / value
 
     ablation = None
     if not args.no_ablation:

@@ -37,15 +37,15 @@ template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false>; };
 
-template <typename T, int N>
-int launch(const T *q, const T *phi, const T *geom, const T *D, int64_t nelem, T *rhs,
-           hipStream_t stream)
+template <typename T, int N, bool SURF>
+int launch(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,
+           int64_t nelem, T *rhs, hipStream_t stream)
 {
     using C = typename Launch<T, N>::C;
     const int64_t blocks = (nelem + C::EPB - 1) / C::EPB;
     if (blocks > INT32_MAX) return ESDG_ERR_NELEM;
-    hipLaunchKernelGGL((volume_rhs_kernel<T, N, C>), dim3((unsigned)blocks), dim3(C::NT), 0,
-                       stream, q, phi, geom, D, nelem, rhs);
+    hipLaunchKernelGGL((volume_rhs_kernel<T, N, C, SURF>), dim3((unsigned)blocks), dim3(C::NT),
+                       0, stream, q, phi, geom, D, nbr, nelem, rhs);
     return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
 }
 
@@ -55,14 +55,16 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-template <typename T>
-int volume_rhs(const T *q, const T *phi, const T *geom, const T *D, int N, int64_t nelem, T *rhs,
-               hipStream_t stream)
+// Both entry points: SURF = false gives the volume term, SURF = true the
+// volume term plus the surface term (nbr must then be given).
+template <typename T, bool SURF>
+int evaluate(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr, int N,
+             int64_t nelem, T *rhs, hipStream_t stream)
 {
     if (N < kMinOrder || N > kMaxOrder) return ESDG_ERR_ORDER;
     if (nelem < 0) return ESDG_ERR_NELEM;
     if (nelem == 0) return ESDG_OK;
-    if (!q || !phi || !geom || !D || !rhs) return ESDG_ERR_NULL;
+    if (!q || !phi || !geom || !D || !rhs || (SURF && !nbr)) return ESDG_ERR_NULL;
     const int64_t Nq = N + 1, Np = Nq * Nq * Nq;
     // the largest array has 10 * nelem * Np elements of T
     if (nelem > INT64_MAX / (10 * Np * (int64_t)sizeof(T))) return ESDG_ERR_NELEM;
@@ -70,17 +72,18 @@ int volume_rhs(const T *q, const T *phi, const T *geom, const T *D, int N, int64
     const int64_t rbytes = 5 * field;
     if (overlaps(rhs, rbytes, q, 5 * field) || overlaps(rhs, rbytes, phi, field) ||
         overlaps(rhs, rbytes, geom, 10 * field) ||
-        overlaps(rhs, rbytes, D, Nq * Nq * (int64_t)sizeof(T)))
+        overlaps(rhs, rbytes, D, Nq * Nq * (int64_t)sizeof(T)) ||
+        (SURF && overlaps(rhs, rbytes, nbr, 6 * nelem * (int64_t)sizeof(int32_t))))
         return ESDG_ERR_ALIAS;
     switch (N) {
-        case 1: return launch<T, 1>(q, phi, geom, D, nelem, rhs, stream);
-        case 2: return launch<T, 2>(q, phi, geom, D, nelem, rhs, stream);
-        case 3: return launch<T, 3>(q, phi, geom, D, nelem, rhs, stream);
-        case 4: return launch<T, 4>(q, phi, geom, D, nelem, rhs, stream);
-        case 5: return launch<T, 5>(q, phi, geom, D, nelem, rhs, stream);
-        case 6: return launch<T, 6>(q, phi, geom, D, nelem, rhs, stream);
-        case 7: return launch<T, 7>(q, phi, geom, D, nelem, rhs, stream);
-        case 8: return launch<T, 8>(q, phi, geom, D, nelem, rhs, stream);
+        case 1: return launch<T, 1, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 2: return launch<T, 2, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 3: return launch<T, 3, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 4: return launch<T, 4, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 5: return launch<T, 5, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 6: return launch<T, 6, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 7: return launch<T, 7, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 8: return launch<T, 8, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
     }
     return ESDG_ERR_ORDER;
 }
@@ -93,13 +96,25 @@ extern "C" {
 int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom, const double *D,
                         int N, int64_t nelem, double *rhs, hipStream_t stream)
 {
-    return esdg::volume_rhs<double>(q, phi, geom, D, N, nelem, rhs, stream);
+    return esdg::evaluate<double, false>(q, phi, geom, D, nullptr, N, nelem, rhs, stream);
 }
 
 int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom, const float *D,
                         int N, int64_t nelem, float *rhs, hipStream_t stream)
 {
-    return esdg::volume_rhs<float>(q, phi, geom, D, N, nelem, rhs, stream);
+    return esdg::evaluate<float, false>(q, phi, geom, D, nullptr, N, nelem, rhs, stream);
+}
+
+int esdg_rhs_f64(const double *q, const double *phi, const double *geom, const double *D,
+                 const int32_t *nbr, int N, int64_t nelem, double *rhs, hipStream_t stream)
+{
+    return esdg::evaluate<double, true>(q, phi, geom, D, nbr, N, nelem, rhs, stream);
+}
+
+int esdg_rhs_f32(const float *q, const float *phi, const float *geom, const float *D,
+                 const int32_t *nbr, int N, int64_t nelem, float *rhs, hipStream_t stream)
+{
+    return esdg::evaluate<float, true>(q, phi, geom, D, nbr, N, nelem, rhs, stream);
 }
 
 const char *esdg_status_string(int status)

@@ -353,6 +353,34 @@ struct NodeLoads {
     }
 };
 
+// Per-node values the pairs use (primitives, scaled b, logs, 1/b, w), from the
+// conserved state and phi.  Phase A stages them for the element's own nodes;
+// the surface term builds them for the face partners in a neighbouring
+// element with the same operations, so both sides of a face see identical
+// values.
+template <typename T>
+__device__ inline NodeRegs<T> node_values(T rho, T m1, T m2, T m3, T E, T ph)
+{
+    using A = Arith<T>;
+    const T gm1 = T(kGamma - 1.0);
+    const T bscale = T(kBScale);
+    NodeRegs<T> V;
+    const T irho = A::rcp(rho);
+    V.rho = rho;
+    V.u1 = m1 * irho;
+    V.u2 = m2 * irho;
+    V.u3 = m3 * irho;
+    const T usq = V.u1 * V.u1 + V.u2 * V.u2 + V.u3 * V.u3;
+    const T p = gm1 * (E - T(0.5) * (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - rho * ph);
+    V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
+    V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
+    V.lrho = A::node_log(rho);
+    V.lb = A::node_log(V.b);
+    V.ph = ph;
+    V.w = ph - T(0.5) * usq;
+    return V;
+}
+
 // Phase A compute: per-node primitives and logs into LDS; returns -1/J per node.
 template <typename T, int N, class C>
 __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C> &B, T *lds,
@@ -360,30 +388,22 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
 {
     using A = Arith<T>;
     constexpr int NODES = Shape<N, C>::kNodes;
-    const T gm1 = T(kGamma - 1.0);
-    const T bscale = T(kBScale);
 #pragma unroll
     for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
-            const T rho = L.v[it][0], E = L.v[it][4], ph = L.v[it][5];
-            const T m1 = L.v[it][1], m2 = L.v[it][2], m3 = L.v[it][3];
-            const T irho = A::rcp(rho);
-            const T u1 = m1 * irho, u2 = m2 * irho, u3 = m3 * irho;
-            const T usq = u1 * u1 + u2 * u2 + u3 * u3;
-            const T p = gm1 * (E - T(0.5) * (m1 * u1 + m2 * u2 + m3 * u3) - rho * ph);
-            const T b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
-            const T ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
-            lds[kRho * NODES + t] = rho;
-            lds[kU1 * NODES + t] = u1;
-            lds[kU2 * NODES + t] = u2;
-            lds[kU3 * NODES + t] = u3;
-            lds[kB * NODES + t] = b;
-            lds[kLogRho * NODES + t] = A::node_log(rho);
-            lds[kLogB * NODES + t] = A::node_log(b);
-            lds[kPhi * NODES + t] = ph;
-            lds[kW * NODES + t] = ph - T(0.5) * usq;
-            lds[kInvB * NODES + t] = ib;
+            const NodeRegs<T> V = node_values(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
+                                              L.v[it][4], L.v[it][5]);
+            lds[kRho * NODES + t] = V.rho;
+            lds[kU1 * NODES + t] = V.u1;
+            lds[kU2 * NODES + t] = V.u2;
+            lds[kU3 * NODES + t] = V.u3;
+            lds[kB * NODES + t] = V.b;
+            lds[kLogRho * NODES + t] = V.lrho;
+            lds[kLogB * NODES + t] = V.lb;
+            lds[kPhi * NODES + t] = V.ph;
+            lds[kW * NODES + t] = V.w;
+            lds[kInvB * NODES + t] = V.ib;
             if constexpr (C::kMetricInLds) {
 #pragma unroll
                 for (int j = 0; j < 9; ++j) lds[(kJa + j) * NODES + t] = L.m[it][j];
@@ -391,6 +411,87 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
             mJ[it] = -A::rcp(L.J[it]);
             if constexpr (C::kFinalizeInLine) lds[Shape<N, C>::kMinusInvJ * NODES + t] = mJ[it];
         }
+    }
+}
+
+// Surface term, fused into the line tasks: the two ends of a direction-k line
+// lie on the element's -xi_k and +xi_k faces, and the line thread adds the
+// face flux of each end to that end's accumulator.
+//
+// Face neighbours come from nbr[nelem][6] (faces -xi1, +xi1, -xi2, +xi2,
+// -xi3, +xi3): the neighbour holds the matching node on its opposite face,
+// at the other end of the same line (conforming faces, same orientation);
+// kFaceWall marks a slip wall, whose partner is the mirror state of the own
+// node (velocity reflected in the face normal Ja^k).
+constexpr int32_t kFaceWall = -1;
+
+template <typename T>
+struct FaceLoads {
+    int32_t nb[2];   // neighbour across the face at line end 0 (a = 0) and end 1 (a = N)
+    T v[2][6];       // its matching node: 5 conserved fields and phi
+    __device__ inline void issue_neighbours(const int32_t *__restrict__ nbr, int64_t e, int k) {
+        nb[0] = nbr[6 * e + 2 * k];
+        nb[1] = nbr[6 * e + 2 * k + 1];
+    }
+    // Loads of the matching nodes; `local0` is the line's first node within
+    // its element, `step` the node stride along the line.  Indices outside
+    // [0, nelem) load nothing.
+    template <int N>
+    __device__ inline void issue_states(const T *__restrict__ q, const T *__restrict__ phi,
+                                        int64_t fstride, int64_t nelem, int local0, int step) {
+        constexpr int Np = (N + 1) * (N + 1) * (N + 1);
+#pragma unroll
+        for (int end = 0; end < 2; ++end) {
+            if (nb[end] >= 0 && nb[end] < nelem) {
+                const int64_t g = (int64_t)nb[end] * Np + local0 + (end == 0 ? N : 0) * step;
+#pragma unroll
+                for (int f = 0; f < 5; ++f) v[end][f] = q[f * fstride + g];
+                v[end][5] = phi[g];
+            }
+        }
+    }
+};
+
+template <typename T, int N, class C>
+__device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
+                                    const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
+                                    const FaceLoads<T> &F, int64_t nelem, T (&acc)[N + 1][5])
+{
+    using A = Arith<T>;
+    constexpr int NODES = Shape<N, C>::kNodes;
+    // The surface term at an end node is -(+-1) Ja^k . F*(own, partner) / (w_end J)
+    // with the LGL end weight w_end = 2/(N(N+1)); pair_update contracts with
+    // Ja^k(own) + Ja^k(partner) = 2 Ja^k(own), so the coefficient is
+    // +-1/(2 w_end) = +-N(N+1)/4.
+    constexpr double kEnd = N * (N + 1) / 4.0;
+#pragma unroll
+    for (int end = 0; end < 2; ++end) {
+        const int a = end ? N : 0;
+        NodeRegs<T> X;
+        X.load_state(lds, NODES, L.nb + a * L.step);
+        if constexpr (C::kMetricInLds) {
+            X.load_metric(lds, NODES, L.nb + a * L.step, L.k);
+        } else {
+            X.n1 = lm[a][0]; X.n2 = lm[a][1]; X.n3 = lm[a][2];
+        }
+        const int32_t nb = F.nb[end];
+        NodeRegs<T> Y = X;
+        if (nb == kFaceWall) {
+            const T nn = X.n1 * X.n1 + X.n2 * X.n2 + X.n3 * X.n3;
+            const T un2 = T(2) * (X.u1 * X.n1 + X.u2 * X.n2 + X.u3 * X.n3) * A::rcp(nn);
+            Y.u1 = X.u1 - un2 * X.n1;
+            Y.u2 = X.u2 - un2 * X.n2;
+            Y.u3 = X.u3 - un2 * X.n3;
+        } else if (nb >= 0 && nb < nelem) {
+            Y = node_values(F.v[end][0], F.v[end][1], F.v[end][2], F.v[end][3], F.v[end][4],
+                            F.v[end][5]);
+            Y.n1 = X.n1; Y.n2 = X.n2; Y.n3 = X.n3;
+        } else {
+            Y.rho = T(__builtin_nan(""));  // invalid neighbour index: the result says so
+        }
+        const T coef = end ? T(kEnd) : T(-kEnd);
+        T partner[5] = {T(0), T(0), T(0), T(0), T(0)};
+        pair_update(X, Y, &coef, &coef, acc[a], partner);
     }
 }
 
@@ -501,12 +602,14 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
     }
 }
 
-// One workgroup per batch of EPB elements.
-template <typename T, int N, class C>
+// One workgroup per batch of EPB elements.  SURF adds the entropy-conservative
+// surface term (face neighbours from nbr), giving the whole right-hand side.
+template <typename T, int N, class C, bool SURF = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
 __attribute__((amdgpu_waves_per_eu(C::WAVES > 0 ? C::WAVES : 1)))
 volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
-                  const T *__restrict__ D, int64_t nelem, T *__restrict__ rhs)
+                  const T *__restrict__ D, const int32_t *__restrict__ nbr, int64_t nelem,
+                  T *__restrict__ rhs)
 {
     using S = Shape<N, C>;
     constexpr int Nq = N + 1;
@@ -517,6 +620,10 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     const bool active = L.active(B.nvalid);
 
     // phase A: issue every global load first
+    FaceLoads<T> face;
+    if constexpr (SURF) {
+        if (active) face.issue_neighbours(nbr, (int64_t)blockIdx.x * C::EPB + L.eb, L.k);
+    }
     NodeLoads<T, N, C> ld;
     ld.issue(q, phi, geom, fstride, B);
     T lm[C::kMetricInLds ? 1 : Nq][3];
@@ -529,6 +636,9 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
                     lm[a][j] = geom[(3 * L.k + j) * fstride + B.g0 + L.nb + a * L.step];
         }
     }
+    if constexpr (SURF) {
+        if (active) face.template issue_states<N>(q, phi, fstride, nelem, L.nb - L.eb * S::Np, L.step);
+    }
     T mJ[S::kNodeIters];
     stage_nodes<T, N, C>(ld, B, lds, mJ);
     __syncthreads();
@@ -539,6 +649,10 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     for (int a = 0; a < Nq; ++a)
 #pragma unroll
         for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
+    // the face partners first: their loaded states die before the pair loop
+    if constexpr (SURF) {
+        if (active) surface_ends<T, N, C>(lds, L, lm, face, nelem, acc);
+    }
     if (active) line_pairs<T, N, C>(lds, D, L, lm, acc);
     __syncthreads();  // node values are dead from here on: LDS becomes the partials
 
@@ -549,52 +663,6 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
         finish_line<T, N, C>(lds, L, active, B, fstride, acc, rhs);
     } else {
         store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
-    }
-}
-
-// Persistent variant: the grid holds only resident workgroups; each walks
-// batches blockIdx.x, blockIdx.x + gridDim.x, ... and loads the next batch's
-// node data into registers while it evaluates the pairs of the current one,
-// so HBM traffic overlaps the pair arithmetic.
-template <typename T, int N, class C>
-__global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
-__attribute__((amdgpu_waves_per_eu(C::WAVES > 0 ? C::WAVES : 1)))
-volume_rhs_persistent(const T *__restrict__ q, const T *__restrict__ phi,
-                      const T *__restrict__ geom, const T *__restrict__ D, int64_t nelem,
-                      T *__restrict__ rhs)
-{
-    static_assert(C::kMetricInLds, "the persistent kernel stages the metric in LDS");
-    using S = Shape<N, C>;
-    constexpr int Nq = N + 1;
-    __shared__ T lds[S::kLdsValues];
-    const int64_t fstride = nelem * S::Np;
-    const int64_t nbatch = (nelem + C::EPB - 1) / C::EPB;
-    const LineTask<N, C> L;
-    const T lm[1][3] = {{T(0), T(0), T(0)}};
-
-    int64_t batch = blockIdx.x;  // uniform over the workgroup: whole workgroups exit
-    NodeLoads<T, N, C> ld;
-    if (batch < nbatch) ld.issue(q, phi, geom, fstride, Batch<N, C>(batch, nelem));
-    for (; batch < nbatch; batch += gridDim.x) {
-        const Batch<N, C> B(batch, nelem);
-        const bool active = L.active(B.nvalid);
-        T mJ[S::kNodeIters];
-        stage_nodes<T, N, C>(ld, B, lds, mJ);
-        __syncthreads();
-        const int64_t next = batch + gridDim.x;
-        if (next < nbatch) ld.issue(q, phi, geom, fstride, Batch<N, C>(next, nelem));
-
-        T acc[Nq][5];
-#pragma unroll
-        for (int a = 0; a < Nq; ++a)
-#pragma unroll
-            for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
-        if (active) line_pairs<T, N, C>(lds, D, L, lm, acc);
-        __syncthreads();
-        write_partials<T, N, C>(lds, L, active, acc);
-        __syncthreads();
-        store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
-        __syncthreads();  // partials read before the next batch's node values overwrite them
     }
 }
 

@@ -2,10 +2,12 @@
 the volume term runs in the HIP kernels of libesdg.so; there is no CPU path.
 
 Two levels:
-  * esdg_volume_rhs_f64 / esdg_volume_rhs_f32 / esdg_status_string /
-    esdg_min_order / esdg_max_order -- the C functions of include/esdg.h under
-    the same names (device pointers as Python ints, a status code returned);
-  * volume_rhs(q, phi, geom, D, out=None, stream=None) -- the same call on
+  * esdg_volume_rhs_f64 / esdg_volume_rhs_f32 / esdg_rhs_f64 / esdg_rhs_f32 /
+    esdg_status_string / esdg_min_order / esdg_max_order -- the C functions of
+    include/esdg.h under the same names (device pointers as Python ints, a
+    status code returned);
+  * volume_rhs(q, phi, geom, D, out=None, stream=None) and
+    rhs(q, phi, geom, D, nbr, out=None, stream=None) -- the same calls on
     torch tensors resident on the GPU, raising EsdgError on a bad status.
 """
 from __future__ import annotations
@@ -24,8 +26,8 @@ ESDG_ERR_LAUNCH = -4
 ESDG_ERR_ALIAS = -5
 
 # every symbol include/esdg.h declares
-EXPORTS = ("esdg_volume_rhs_f64", "esdg_volume_rhs_f32", "esdg_status_string",
-           "esdg_min_order", "esdg_max_order")
+EXPORTS = ("esdg_volume_rhs_f64", "esdg_volume_rhs_f32", "esdg_rhs_f64", "esdg_rhs_f32",
+           "esdg_status_string", "esdg_min_order", "esdg_max_order")
 
 
 class EsdgError(RuntimeError):
@@ -55,6 +57,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ci
         fn.argtypes = [vp, vp, vp, vp, ci, i64, vp, vp]
+    for name in ("esdg_rhs_f64", "esdg_rhs_f32"):
+        fn = getattr(lib, name)
+        fn.restype = ci
+        fn.argtypes = [vp, vp, vp, vp, vp, ci, i64, vp, vp]
     lib.esdg_status_string.restype = ctypes.c_char_p
     lib.esdg_status_string.argtypes = [ci]
     lib.esdg_min_order.restype = ci
@@ -77,6 +83,16 @@ def esdg_volume_rhs_f32(q: int, phi: int, geom: int, D: int, N: int, nelem: int,
     return load().esdg_volume_rhs_f32(q, phi, geom, D, N, nelem, rhs, stream)
 
 
+def esdg_rhs_f64(q: int, phi: int, geom: int, D: int, nbr: int, N: int, nelem: int, rhs: int,
+                 stream: int = 0) -> int:
+    return load().esdg_rhs_f64(q, phi, geom, D, nbr, N, nelem, rhs, stream)
+
+
+def esdg_rhs_f32(q: int, phi: int, geom: int, D: int, nbr: int, N: int, nelem: int, rhs: int,
+                 stream: int = 0) -> int:
+    return load().esdg_rhs_f32(q, phi, geom, D, nbr, N, nelem, rhs, stream)
+
+
 def esdg_status_string(status: int) -> str:
     return load().esdg_status_string(status).decode()
 
@@ -97,6 +113,21 @@ def volume_rhs(q, phi, geom, D, out=None, stream=None):
     contiguous torch tensors of one dtype (float64 or float32) on one GPU.
     The call is asynchronous on `stream` (default: torch's current stream).
     """
+    return _call(q, phi, geom, D, None, out, stream)
+
+
+def rhs(q, phi, geom, D, nbr, out=None, stream=None):
+    """rhs[5][nelem][Np] = volume + entropy-conservative surface term on the
+    GPU; nbr [nelem][6] int32 face neighbours on the same GPU (-1 = slip wall),
+    the rest as volume_rhs."""
+    import torch
+
+    if nbr is None or nbr.dtype != torch.int32:
+        raise TypeError("nbr must be an int32 tensor")
+    return _call(q, phi, geom, D, nbr, out, stream)
+
+
+def _call(q, phi, geom, D, nbr, out, stream):
     import torch
 
     dtype = q.dtype
@@ -124,6 +155,11 @@ def volume_rhs(q, phi, geom, D, out=None, stream=None):
         raise ValueError(f"phi must be [{nelem}][{Np}]")
     if tuple(geom.shape) != (10, nelem, Np):
         raise ValueError(f"geom must be [10][{nelem}][{Np}]")
+    if nbr is not None:
+        if not nbr.is_cuda or nbr.device != q.device or not nbr.is_contiguous():
+            raise ValueError(f"nbr must be a contiguous GPU tensor on {q.device}")
+        if tuple(nbr.shape) != (nelem, 6):
+            raise ValueError(f"nbr must be [{nelem}][6]")
     if out is None:
         out = torch.empty_like(q)
     elif (out.dtype != dtype or out.device != q.device or tuple(out.shape) != tuple(q.shape)
@@ -132,10 +168,15 @@ def volume_rhs(q, phi, geom, D, out=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    fn = esdg_volume_rhs_f64 if dtype == torch.float64 else esdg_volume_rhs_f32
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), N, nelem,
-                out.data_ptr(), handle)
+        if nbr is None:
+            fn = esdg_volume_rhs_f64 if dtype == torch.float64 else esdg_volume_rhs_f32
+            st = fn(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), N, nelem,
+                    out.data_ptr(), handle)
+        else:
+            fn = esdg_rhs_f64 if dtype == torch.float64 else esdg_rhs_f32
+            st = fn(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), nbr.data_ptr(),
+                    N, nelem, out.data_ptr(), handle)
     if st != ESDG_OK:
         raise EsdgError(st, esdg_status_string(st))
     return out

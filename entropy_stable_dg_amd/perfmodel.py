@@ -14,6 +14,14 @@ work, not the ordered-pair work the symmetric evaluation avoids):
   per node (primitives, p, b, 2 logs,
             1/b, direction sum, -1/J) ...  38
 Unordered pairs per element: 3 (N+1)^2 (N+1) N / 2.
+
+Whole right-hand side (volume + entropy-conservative surface term, one fused
+kernel): the algorithmic traffic adds only the connectivity, 6 int32 per
+element; the kernel also re-reads each face partner's 5 fields and phi from
+the neighbouring element (48 B per face node in fp64 with a neighbour, none at
+a slip wall), which the cache may or may not serve.  Work per face node: one
+pair (120) plus the partner's per-node values (38) with a neighbour; one pair
+and the mirror state (12) at a slip wall.
 """
 from __future__ import annotations
 
@@ -52,3 +60,35 @@ def algorithmic_bytes(N: int, nelem: int, dtype: str) -> int:
 
 def arithmetic_intensity(N: int, dtype: str) -> float:
     return flops_per_dof(N) / bytes_per_dof(dtype)
+
+
+FLOP_PER_MIRROR = 12
+
+
+def face_nodes_per_element(N: int) -> int:
+    return 6 * (N + 1) ** 2
+
+
+def surface_flops(N: int, nbr) -> int:
+    """FLOP of the surface term over a mesh with connectivity nbr [nelem][6]."""
+    import numpy as np
+
+    nbr = np.asarray(nbr)
+    walls = int((nbr < 0).sum())
+    faces = int(nbr.size)
+    per_face = (N + 1) ** 2
+    return ((faces - walls) * per_face * (FLOP_PER_PAIR + FLOP_PER_NODE)
+            + walls * per_face * (FLOP_PER_PAIR + FLOP_PER_MIRROR))
+
+
+def face_partner_bytes(N: int, nbr, dtype: str) -> int:
+    """Bytes of the face partners' states the fused kernel reads (6 values per
+    face node with a neighbour)."""
+    import numpy as np
+
+    size = 8 if dtype == "f64" else 4
+    return int((np.asarray(nbr) >= 0).sum()) * (N + 1) ** 2 * 6 * size
+
+
+def algorithmic_bytes_rhs(N: int, nelem: int, dtype: str) -> int:
+    return algorithmic_bytes(N, nelem, dtype) + 24 * nelem

@@ -1,6 +1,8 @@
 /*
  * esdg.h -- C ABI of the ESDG flux-differencing volume-term library
- * (libesdg.so, HIP for AMD gfx950).
+ * (libesdg.so, HIP for AMD gfx950): the volume term alone
+ * (esdg_volume_rhs_*) and the whole right-hand side with the
+ * entropy-conservative surface term fused into the same kernel (esdg_rhs_*).
  *
  * The operation is the volume term of the semi-discrete entropy-stable DG
  * form of "GPU Performance of an Entropy-Stable Discontinuous Galerkin Euler
@@ -65,6 +67,40 @@ int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom,
 int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom,
                         const float *D, int N, int64_t nelem, float *rhs,
                         hipStream_t stream);
+
+/*
+ * Whole semi-discrete right-hand side of Eq. 2 of the same page (its volume
+ * term plus its surface term, source h = 0), with the entropy-conservative
+ * two-point flux also on the faces: the face dissipation the page adds to it
+ * ([ESDG-GPU §3], from its reference [56]) is not part of this call.  At a
+ * node on the xi_k = +-1 face of an element the surface term is
+ *     -(+-1) sum_j Ja^k_j(i) F*_j(q_i, q_partner) / (w_end J_i),
+ * w_end = 2/(N(N+1)) the LGL end weight, F* the same two-point flux as in
+ * the volume (gravity term included).
+ *
+ *   nbr  [nelem][6] int32, device: the element across each face, faces in the
+ *        order -xi1, +xi1, -xi2, +xi2, -xi3, +xi3.  A neighbour index e' in
+ *        [0, nelem) means the faces are conforming with the same orientation:
+ *        the partner of node (.., i_k = N, ..) across the +xi_k face is node
+ *        (.., i_k = 0, ..) of e' (same tangential indices), and vice versa;
+ *        periodic meshes simply name the wrapped element.  -1 is a slip wall:
+ *        the partner is the mirror state of the own node (same density,
+ *        pressure and phi, velocity reflected in the face normal Ja^k).  Any
+ *        other value makes the rhs of that face's nodes NaN (the kernel reads
+ *        nothing through it); the library does not check nbr on the host.
+ *
+ * Everything else (layouts, ownership, streams, status codes, rhs
+ * overwritten, nelem == 0 a no-op) as for esdg_volume_rhs_f64; rhs must not
+ * overlap nbr either (ESDG_ERR_ALIAS), and nbr == NULL gives ESDG_ERR_NULL.
+ */
+int esdg_rhs_f64(const double *q, const double *phi, const double *geom,
+                 const double *D, const int32_t *nbr, int N, int64_t nelem,
+                 double *rhs, hipStream_t stream);
+
+/* The same in fp32 arithmetic. */
+int esdg_rhs_f32(const float *q, const float *phi, const float *geom,
+                 const float *D, const int32_t *nbr, int N, int64_t nelem,
+                 float *rhs, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *esdg_status_string(int status);

@@ -105,6 +105,24 @@ def test_alias_errors(fn, size):
     assert fn(A, B, C, Dp, N, nelem, Dp + 8, 0) == esdg.ESDG_ERR_ALIAS
 
 
+@pytest.mark.parametrize("fn,size", [(esdg.esdg_rhs_f64, 8), (esdg.esdg_rhs_f32, 4)])
+def test_rhs_argument_errors(fn, size):
+    NB = 0x60000000
+    assert fn(A, B, C, Dp, NB, 0, 1, R, 0) == esdg.ESDG_ERR_ORDER
+    assert fn(A, B, C, Dp, NB, 4, -1, R, 0) == esdg.ESDG_ERR_NELEM
+    assert fn(0, 0, 0, 0, 0, 4, 0, 0, 0) == esdg.ESDG_OK
+    for i in range(6):
+        args = [A, B, C, Dp, NB, R]
+        args[i] = 0
+        assert fn(args[0], args[1], args[2], args[3], args[4], 4, 10, args[5], 0) == esdg.ESDG_ERR_NULL
+    # rhs overlapping the connectivity array
+    N, nelem = 3, 100
+    assert fn(A, B, C, Dp, NB, N, nelem, NB + 6 * nelem * 4 - size, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, NB, N, nelem, NB - 5 * nelem * 64 * size + size, 0) == esdg.ESDG_ERR_ALIAS
+    # and the inputs, as for the volume term
+    assert fn(A, B, C, Dp, NB, N, nelem, A + 4 * nelem * 64 * size, 0) == esdg.ESDG_ERR_ALIAS
+
+
 def test_tensor_wrapper_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(5, 1, 8, dtype=torch.float64)
@@ -115,3 +133,8 @@ def test_tensor_wrapper_rejects_cpu_tensors():
         esdg.volume_rhs(q, phi, geom, D)
     with pytest.raises(TypeError):
         esdg.volume_rhs(q.float(), phi, geom, D)
+    nbr = torch.zeros(1, 6, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        esdg.rhs(q, phi, geom, D, nbr)
+    with pytest.raises(TypeError):
+        esdg.rhs(q, phi, geom, D, nbr.long())

@@ -1,0 +1,190 @@
+"""GPU parity of the whole right-hand side (volume term + entropy-conservative
+surface term fused into one kernel, esdg_rhs_*) against the CPU oracle, and
+the oracle's global identities re-checked on the GPU output.
+
+Tolerance: the whole right-hand side cancels (face terms of O(p/h) against
+their volume counterparts; a hydrostatic base against its pressure gradient),
+so its error is measured against the size of what cancels: per field,
+max_i |rhs_gpu - rhs_oracle| / max_i mag_i <= 1e-11 (fp64) and 2e-5 (fp32),
+mag_i being the sum of the absolute values of node i's summands (volume and
+surface), as the oracle reports it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import esdg
+from entropy_stable_dg_amd import inputs as I
+from tests.test_gpu_parity import dev, to_gpu
+from tests.test_oracle_pins import entropy_vars, weights3
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float64: 1e-11, np.float32: 2e-5}
+
+
+def gpu_full_rhs(q, phi, geom, D, nbr):
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    tn = torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev())
+    out = esdg.rhs(tq, tp, tg, tD, tn)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_full(got, ref, mag, tol, label):
+    got = got.astype(np.float64)
+    err = [float(np.abs(got[f] - ref[f]).max() / np.abs(mag[f]).max()) for f in range(5)]
+    lit = [float(np.abs(got[f] - ref[f]).max() / max(np.abs(ref[f]).max(), 1e-300)) for f in range(5)]
+    print(f"[rhs] {label}: err/max mag {['%.1e' % e for e in err]}  err/max|rhs| {['%.1e' % e for e in lit]}",
+          flush=True)
+    assert np.all(np.isfinite(got)), label
+    assert max(err) <= tol, (label, err)
+
+
+@pytest.mark.parametrize("name", ["tiny", "bubble", "baroclinic", "high_order"])
+def test_workloads_fp64(name):
+    wl = I.make(name)
+    print(f"[rhs] {name}: N={wl.N} nelem={wl.nelem} periodic={wl.periodic}", flush=True)
+    got = gpu_full_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.nbr)
+    ref, mag = oracle.rhs(wl.q, wl.phi, wl.geom, wl.D, wl.nbr, wl.N, with_magnitude=True)
+    check_full(got, ref, mag, TOL[np.float64], name)
+
+
+@pytest.mark.parametrize("name", ["bubble_f32", "tiny", "baroclinic"])
+def test_workloads_fp32(name):
+    wl = I.make(name)
+    q, phi, geom, D = (a.astype(np.float32) for a in (wl.q, wl.phi, wl.geom, wl.D))
+    got = gpu_full_rhs(q, phi, geom, D, wl.nbr)
+    assert got.dtype == np.float32
+    ref, mag = oracle.rhs(q, phi, geom, D, wl.nbr, wl.N, with_magnitude=True)
+    check_full(got, ref, mag, TOL[np.float32], f"{name} fp32")
+
+
+def random_closed_mesh(N, K, periodic, seed, nodewise=False):
+    rng = np.random.default_rng(seed)
+    D = I.diff_matrix(N)
+    hi = tuple(1000.0 * k for k in K)
+    X = I.box_mesh(K, (0, 0, 0), hi, N, warp_frac=0.05, seed=seed)
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    x, y, z = X.reshape(3, ne, -1)
+    if nodewise:
+        shape = x.shape
+        rho = rng.uniform(0.5, 1.5, shape)
+        u = rng.uniform(-50, 50, (3,) + shape)
+        p = rng.uniform(0.5e5, 1.5e5, shape)
+        phi = rng.uniform(0, 1e4, shape)
+    else:
+        k = rng.uniform(1.0, 3.0, 6) / 1000.0
+        rho = 1.0 + 0.3 * np.sin(k[0] * x + k[1] * y) * np.cos(k[2] * z)
+        u = np.stack([30 * np.sin(k[3] * y + 1e-3 * z), 20 * np.cos(k[4] * x - 1e-3 * y),
+                      10 * np.sin(k[5] * z + 1e-3 * x)])
+        p = 1e5 * (1 + 0.2 * np.cos(k[1] * x + k[2] * z))
+        phi = I.GRAV * z
+    q = I.conserved(rho, u, p, phi)
+    return q, phi, geom, D, I.box_connectivity(K, periodic), (rho, u, p, phi)
+
+
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_every_order(N, dtype):
+    K = (3, 2, 2)
+    periodic = (True, N % 2 == 0, N % 3 != 0)
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, periodic, seed=10 + N)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_full_rhs(q, phi, geom, D, nbr)
+    ref, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    check_full(got, ref, mag, TOL[dtype], f"N={N} {np.dtype(dtype).name} periodic={periodic}")
+
+
+@pytest.mark.parametrize("K", [(7, 1, 1), (5, 1, 2), (1, 1, 1)])
+def test_ragged_and_self_neighbour_meshes(K):
+    """Element counts that leave the last workgroup partly empty, and a single
+    element that is its own neighbour across every periodic face."""
+    N = 4
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, (True, True, True), seed=sum(K))
+    got = gpu_full_rhs(q, phi, geom, D, nbr)
+    ref, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    check_full(got, ref, mag, TOL[np.float64], f"K={K}")
+
+
+@pytest.mark.parametrize("N,periodic", [(3, (True, True, True)), (4, (True, False, False)),
+                                        (7, (False, True, False))])
+def test_global_entropy_conservation_on_gpu(N, periodic):
+    """sum_e sum_i w_i J_i v_i . rhs_i = 0 for the GPU's rhs (nodewise random
+    state, curved mesh, periodic faces and slip walls)."""
+    K = (3, 2, 2)
+    q, phi, geom, D, nbr, (rho, u, p, ph) = random_closed_mesh(N, K, periodic, seed=30 + N,
+                                                              nodewise=True)
+    got = gpu_full_rhs(q, phi, geom, D, nbr)
+    W, _ = weights3(N)
+    total, scale = 0.0, 0.0
+    for e in range(rho.shape[0]):
+        v = entropy_vars(rho[e], u[:, e], p[e], ph[e])
+        terms = W[:, None] * geom[9, e][:, None] * v * got[:, e, :].T
+        total += terms.sum()
+        scale += np.abs(terms).sum()
+    print(f"[rhs] entropy rate N={N}: {total:.3e} of {scale:.3e}", flush=True)
+    assert abs(total) <= 1e-12 * scale
+    # mass and total energy, against the summed magnitudes of their terms
+    _, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    wj = W[None, :] * geom[9]
+    for f in (0, 4):
+        assert abs((wj * got[f]).sum()) <= 1e-12 * (wj * mag[f]).sum()
+
+
+def test_hydrostatic_balance_on_gpu():
+    """Isothermal atmosphere at rest between slip walls on a curved mesh: the
+    GPU's whole right-hand side vanishes to round-off."""
+    N, K = 4, (2, 2, 3)
+    D = I.diff_matrix(N)
+    X = I.box_mesh(K, (0, 0, 0), (2000, 2000, 3000), N, warp_frac=0.05, seed=4)
+    geom = I.metrics(X, D)
+    ne = X.shape[1]
+    z = X.reshape(3, ne, -1)[2]
+    phi = I.GRAV * z
+    p = I.P0 * np.exp(-phi / (I.R_GAS * 300.0))
+    rho = p / (I.R_GAS * 300.0)
+    q = I.conserved(rho, np.zeros((3,) + rho.shape), p, phi)
+    nbr = I.box_connectivity(K, (True, True, False))
+    got = gpu_full_rhs(q, phi, geom, D, nbr)
+    _, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    for f in range(5):
+        m = np.abs(mag[f]).max()
+        if m == 0.0:   # density and energy fluxes vanish identically at rest
+            assert np.all(got[f] == 0.0), f
+            continue
+        r = np.abs(got[f]).max() / m
+        print(f"[rhs] hydrostatic field {f}: max|rhs|/max mag = {r:.2e}", flush=True)
+        assert r <= 1e-13
+
+
+def test_invalid_neighbour_gives_nan_on_that_face_only():
+    N, K = 3, (3, 1, 1)
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, (True, False, False), seed=7)
+    good = gpu_full_rhs(q, phi, geom, D, nbr)
+    bad_nbr = nbr.copy()
+    bad_nbr[1, 1] = 3           # +xi1 face of element 1: index == nelem (invalid)
+    bad_nbr[2, 4] = -7          # -xi3 face of element 2: below -1 (invalid)
+    got = gpu_full_rhs(q, phi, geom, D, bad_nbr)
+    Nq = N + 1
+    n = np.arange(Nq ** 3)                  # n = a + Nq (b + Nq c)
+    aa, cc = n % Nq, n // (Nq * Nq)
+    bad = np.zeros(good.shape[1:], dtype=bool)
+    bad[1] = aa == N
+    bad[2] = cc == 0
+    assert np.all(np.isnan(got[:, bad]))
+    assert np.array_equal(got[:, ~bad], good[:, ~bad])
+
+
+def test_volume_entry_unchanged_by_surface_build():
+    """esdg_volume_rhs_* still gives the volume term alone: on a mesh whose
+    faces all cancel exactly (a constant state), volume + surface is ~0 while
+    the volume term alone is not."""
+    wl = I.make("tiny")
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    vol = esdg.volume_rhs(tq, tp, tg, tD).cpu().numpy()
+    ref = oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)
+    for f in range(5):
+        assert np.abs(vol[f] - ref[f]).max() <= 1e-11 * np.abs(ref[f]).max()

@@ -125,3 +125,68 @@ def test_indices_in_bounds(dtype, N, nelem):
                     assert a * Nq + l < Nq2 and l * Nq + a < Nq2    # D reads
     assert np.all(written == 1)
     assert np.all(out_written == 1)
+
+
+@pytest.mark.parametrize("dtype", ["double", "float"])
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("K,periodic", [((1, 1, 1), (True, True, True)),
+                                        ((3, 2, 1), (True, False, True)),
+                                        ((2, 3, 2), (False, False, False))])
+def test_face_partner_indices(dtype, N, K, periodic):
+    """Surface term of the whole right-hand side: each line thread's two ends
+    read the neighbour index of faces 2k and 2k+1 of its own element and load
+    the matching node of that neighbour, the other end of the same line:
+    in bounds, on the opposite face, same tangential indices; every
+    (element, face, face node) is handled by exactly one line end."""
+    from entropy_stable_dg_amd import inputs as I
+
+    EPB, NT, _, dirmajor, _ = launch_table()[(dtype, N)]
+    Nq = N + 1
+    Nq2, Np = Nq * Nq, Nq ** 3
+    nbr = I.box_connectivity(K, periodic)
+    nelem = nbr.shape[0]
+    lines = 3 * EPB * Nq2
+    blocks = (nelem + EPB - 1) // EPB
+    seen = np.zeros((nelem, 6, Nq2), dtype=int)
+
+    def abc(n):
+        return n % Nq, (n // Nq) % Nq, n // Nq2
+
+    for blk in range(blocks):
+        nvalid = min(EPB, nelem - blk * EPB) * Np
+        for task in range(NT):
+            if dirmajor:
+                k = task // (EPB * Nq2)
+                r = task - k * EPB * Nq2
+                eb = r // Nq2
+                line = r - eb * Nq2
+                if k > 2:
+                    k, eb = 2, EPB
+            else:
+                eb = task // (3 * Nq2)
+                r3 = task - eb * 3 * Nq2
+                k = r3 // Nq2
+                line = r3 - k * Nq2
+            if not (task < lines and eb * Np < nvalid):
+                continue
+            p1, p2 = line % Nq, line // Nq
+            base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
+            step = [1, Nq, Nq2][k]
+            e = blk * EPB + eb
+            assert 0 <= 6 * e + 2 * k + 1 < 6 * nelem
+            for end in (0, 1):
+                a = N if end else 0
+                own = base + a * step
+                face = 2 * k + end
+                nb = nbr[e, face]
+                tang = [x for i, x in enumerate(abc(own)) if i != k]
+                seen[e, face, tang[0] + Nq * tang[1]] += 1
+                if nb < 0:
+                    continue
+                partner = base + (N if end == 0 else 0) * step
+                g = nb * Np + partner
+                assert 0 <= g < nelem * Np and 4 * nelem * Np + g < 5 * nelem * Np
+                pa = abc(partner)
+                assert pa[k] == N - abc(own)[k]
+                assert [x for i, x in enumerate(pa) if i != k] == tang
+    assert np.all(seen == 1)
