@@ -68,6 +68,8 @@ class Oracle:
         lib.oracle_surface_rhs.restype = ctypes.c_int
         lib.oracle_surface_rhs.argtypes = [_P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                            ctypes.c_int64, _P, _P, ctypes.c_int]
+        lib.oracle_add_coriolis.restype = None
+        lib.oracle_add_coriolis.argtypes = [_P, _P, ctypes.c_int64, _P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         self.lib = lib
@@ -123,14 +125,29 @@ class Oracle:
             raise ValueError(f"oracle_surface_rhs failed ({rc})")
         return rhs
 
-    def rhs(self, q, phi, geom, D, nbr, N: int, *, with_magnitude: bool = False,
+    def rhs(self, q, phi, geom, D, nbr, N: int, *, omega=None, with_magnitude: bool = False,
             threads: int = 0):
-        """Whole semi-discrete right-hand side (volume + entropy-conservative
-        surface term, h = 0)."""
+        """Whole semi-discrete right-hand side: volume + entropy-conservative
+        surface term + the Coriolis source -omega x U (omega None: h = 0)."""
         out = self.volume_rhs(q, phi, geom, D, N, with_magnitude=with_magnitude, threads=threads)
         rhs, mag = out if with_magnitude else (out, None)
         self.surface_rhs(q, phi, geom, nbr, N, rhs=rhs, mag=mag, threads=threads)
+        if omega is not None:
+            self.add_coriolis(q, omega, rhs)
+            if mag is not None:
+                h = np.zeros_like(rhs)
+                self.add_coriolis(q, omega, h)
+                mag += np.abs(h)
         return (rhs, mag) if with_magnitude else rhs
+
+    def add_coriolis(self, q, omega, rhs):
+        """rhs[1:4] -= omega x U at every node (in place); q, rhs [5][...]."""
+        q = _f64(q)
+        om = _f64(omega).reshape(3)
+        if rhs.dtype != np.float64 or not rhs.flags.c_contiguous or rhs.shape != q.shape:
+            raise ValueError("rhs must be a contiguous float64 array shaped like q")
+        self.lib.oracle_add_coriolis(_ptr(q), _ptr(om), q.size // 5, _ptr(rhs))
+        return rhs
 
     def ec_flux(self, qi, phii, ql, phil, j: int) -> np.ndarray:
         """Two-point flux F_j(q_i, q_l) for a batch of pairs: qi, ql [n][5]

@@ -19,6 +19,7 @@
  *   surface term ......................... [ESDG-GPU §3, Eq. 2 (second brace) and the text
  *                                           after it: minus side = own element, plus side =
  *                                           the neighbour]
+ *   Coriolis source h = -omega x U ....... [ESDG-GPU §2, Eq. 1b; §3, h in Eq. 2]
  *
  * Readings of the pages that this file takes (the pages print the momentum
  * component only; the other components are fixed by entropy conservation,
@@ -313,6 +314,24 @@ int oracle_surface_rhs(const double *q, const double *phi, const double *geom,
         }
     }
     return 0;
+}
+
+/*
+ * Source term h of Eq. 2 from the Coriolis term of Eq. 1b: h = -omega x U on
+ * the momentum components, U = (q1, q2, q3) the momentum, omega the rotation
+ * vector as Eq. 1b writes it (for a planet rotating at Omega it is 2 Omega).
+ * ADDED to rhs at every node; density and energy get nothing.
+ */
+void oracle_add_coriolis(const double *q, const double omega[3], int64_t nnodes, double *rhs)
+{
+    const int64_t stride = nnodes;
+    for (int64_t n = 0; n < nnodes; ++n) {
+        const double U[3] = {q[1 * stride + n], q[2 * stride + n], q[3 * stride + n]};
+        const double wxU[3] = {omega[1] * U[2] - omega[2] * U[1],
+                               omega[2] * U[0] - omega[0] * U[2],
+                               omega[0] * U[1] - omega[1] * U[0]};
+        for (int m = 0; m < 3; ++m) rhs[(1 + m) * stride + n] -= wxU[m];
+    }
 }
 
 /* Threads the OpenMP runtime would use by default (1 without OpenMP). */

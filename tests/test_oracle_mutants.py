@@ -8,6 +8,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as P
 from tests import test_oracle_surface as S
+from tests import test_oracle_coriolis as R
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "esdg_oracle.c")
 
@@ -59,6 +60,11 @@ MUTANTS = [
      "/ (n[0] * n[0] + n[1] * n[1] + n[2] * n[2]);", ";"),
     ("surface term without 1/J",
      "(double)side * term[f] / (w_end * Ji);", "(double)side * term[f] / w_end;"),
+    # Coriolis source
+    ("Coriolis term with the wrong sign",
+     "rhs[(1 + m) * stride + n] -= wxU[m];", "rhs[(1 + m) * stride + n] += wxU[m];"),
+    ("Coriolis cross product with swapped components",
+     "omega[2] * U[0] - omega[0] * U[2]", "omega[0] * U[2] - omega[2] * U[0]"),
 ]
 
 # a cheap battery of pins: every check raises AssertionError on a mismatch
@@ -77,6 +83,7 @@ BATTERY = [
     (S.check_free_stream_full, (2, (True, True, True))),
     (S.check_hydrostatic_full, (3, 0.05)),
     (S.check_surface_vs_50_digits, (1,)),
+    (R.check_f_plane, ()), (R.check_general_omega, ()),
 ]
 
 
