@@ -91,7 +91,7 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
         for i in range(k):
             p = ptrs[i % nsets] if rotate else ptrs[0]
             if full:
-                st = fn(p[0], p[1], p[2], p[3], p[4], N, nelem, p[5], handle)
+                st = fn(p[0], p[1], p[2], p[3], p[4], None, N, nelem, p[5], handle)
             else:
                 st = fn(p[0], p[1], p[2], p[3], N, nelem, p[5], handle)
             if st != 0:

@@ -39,13 +39,13 @@ template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false>; };
 
 template <typename T, int N, bool SURF>
 int launch(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,
-           int64_t nelem, T *rhs, hipStream_t stream)
+           Rotation<T> rot, int64_t nelem, T *rhs, hipStream_t stream)
 {
     using C = typename Launch<T, N>::C;
     const int64_t blocks = (nelem + C::EPB - 1) / C::EPB;
     if (blocks > INT32_MAX) return ESDG_ERR_NELEM;
     hipLaunchKernelGGL((volume_rhs_kernel<T, N, C, SURF>), dim3((unsigned)blocks), dim3(C::NT),
-                       0, stream, q, phi, geom, D, nbr, nelem, rhs);
+                       0, stream, q, phi, geom, D, nbr, rot, nelem, rhs);
     return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
 }
 
@@ -56,10 +56,11 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 }
 
 // Both entry points: SURF = false gives the volume term, SURF = true the
-// volume term plus the surface term (nbr must then be given).
+// volume term plus the surface term (nbr must then be given) and, with omega
+// given (host pointer, 3 values read during the call), the Coriolis source.
 template <typename T, bool SURF>
-int evaluate(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr, int N,
-             int64_t nelem, T *rhs, hipStream_t stream)
+int evaluate(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,
+             const T *omega, int N, int64_t nelem, T *rhs, hipStream_t stream)
 {
     if (N < kMinOrder || N > kMaxOrder) return ESDG_ERR_ORDER;
     if (nelem < 0) return ESDG_ERR_NELEM;
@@ -75,15 +76,17 @@ int evaluate(const T *q, const T *phi, const T *geom, const T *D, const int32_t 
         overlaps(rhs, rbytes, D, Nq * Nq * (int64_t)sizeof(T)) ||
         (SURF && overlaps(rhs, rbytes, nbr, 6 * nelem * (int64_t)sizeof(int32_t))))
         return ESDG_ERR_ALIAS;
+    Rotation<T> rot{T(0), T(0), T(0), false};
+    if (SURF && omega) rot = Rotation<T>{omega[0], omega[1], omega[2], true};
     switch (N) {
-        case 1: return launch<T, 1, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 2: return launch<T, 2, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 3: return launch<T, 3, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 4: return launch<T, 4, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 5: return launch<T, 5, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 6: return launch<T, 6, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 7: return launch<T, 7, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
-        case 8: return launch<T, 8, SURF>(q, phi, geom, D, nbr, nelem, rhs, stream);
+        case 1: return launch<T, 1, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 2: return launch<T, 2, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 3: return launch<T, 3, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 4: return launch<T, 4, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 5: return launch<T, 5, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 6: return launch<T, 6, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 7: return launch<T, 7, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
+        case 8: return launch<T, 8, SURF>(q, phi, geom, D, nbr, rot, nelem, rhs, stream);
     }
     return ESDG_ERR_ORDER;
 }
@@ -96,25 +99,27 @@ extern "C" {
 int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom, const double *D,
                         int N, int64_t nelem, double *rhs, hipStream_t stream)
 {
-    return esdg::evaluate<double, false>(q, phi, geom, D, nullptr, N, nelem, rhs, stream);
+    return esdg::evaluate<double, false>(q, phi, geom, D, nullptr, nullptr, N, nelem, rhs, stream);
 }
 
 int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom, const float *D,
                         int N, int64_t nelem, float *rhs, hipStream_t stream)
 {
-    return esdg::evaluate<float, false>(q, phi, geom, D, nullptr, N, nelem, rhs, stream);
+    return esdg::evaluate<float, false>(q, phi, geom, D, nullptr, nullptr, N, nelem, rhs, stream);
 }
 
 int esdg_rhs_f64(const double *q, const double *phi, const double *geom, const double *D,
-                 const int32_t *nbr, int N, int64_t nelem, double *rhs, hipStream_t stream)
+                 const int32_t *nbr, const double *omega, int N, int64_t nelem, double *rhs,
+                 hipStream_t stream)
 {
-    return esdg::evaluate<double, true>(q, phi, geom, D, nbr, N, nelem, rhs, stream);
+    return esdg::evaluate<double, true>(q, phi, geom, D, nbr, omega, N, nelem, rhs, stream);
 }
 
 int esdg_rhs_f32(const float *q, const float *phi, const float *geom, const float *D,
-                 const int32_t *nbr, int N, int64_t nelem, float *rhs, hipStream_t stream)
+                 const int32_t *nbr, const float *omega, int N, int64_t nelem, float *rhs,
+                 hipStream_t stream)
 {
-    return esdg::evaluate<float, true>(q, phi, geom, D, nbr, N, nelem, rhs, stream);
+    return esdg::evaluate<float, true>(q, phi, geom, D, nbr, omega, N, nelem, rhs, stream);
 }
 
 const char *esdg_status_string(int status)

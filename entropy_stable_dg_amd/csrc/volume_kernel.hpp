@@ -546,6 +546,23 @@ __device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const L
     }
 }
 
+// Source term h of the whole right-hand side: the Coriolis term of the
+// momentum equation, h = -omega x U (U the momentum).  `on` is uniform over
+// the launch; the momentum is re-read at the store (the workgroup loaded it
+// in phase A, so it comes from cache).
+template <typename T>
+struct Rotation {
+    T w1, w2, w3;
+    bool on;
+    __device__ inline void add(const T *__restrict__ q, int64_t fstride, int64_t g,
+                               T &h1, T &h2, T &h3) const {
+        const T U1 = q[fstride + g], U2 = q[2 * fstride + g], U3 = q[3 * fstride + g];
+        h1 -= w2 * U3 - w3 * U2;
+        h2 -= w3 * U1 - w1 * U3;
+        h3 -= w1 * U2 - w2 * U1;
+    }
+};
+
 // Phases C and D: directional partials through LDS, scaling, store.
 template <typename T, int N, class C>
 __device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool active,
@@ -567,7 +584,8 @@ __device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool acti
 template <typename T, int N, class C>
 __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool active,
                                    const Batch<N, C> &B, int64_t fstride,
-                                   const T (&acc)[N + 1][5], T *__restrict__ rhs)
+                                   const T (&acc)[N + 1][5], const T *__restrict__ q,
+                                   const Rotation<T> &rot, T *__restrict__ rhs)
 {
     constexpr int NODES = Shape<N, C>::kNodes;
     if (active && L.k == 2) {
@@ -576,16 +594,21 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
             const int s = L.nb + a * L.step;
             const T mJ = lds[Shape<N, C>::kMinusInvJ * NODES + s];
             const int64_t g = B.g0 + s;
+            T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f)
-                rhs[f * fstride + g] = (lds[f * NODES + s] + lds[(5 + f) * NODES + s] + acc[a][f]) * mJ;
+                r[f] = (lds[f * NODES + s] + lds[(5 + f) * NODES + s] + acc[a][f]) * mJ;
+            if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
+#pragma unroll
+            for (int f = 0; f < 5; ++f) rhs[f * fstride + g] = r[f];
         }
     }
 }
 
 template <typename T, int N, class C>
 __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fstride,
-                                 const T (&mJ)[Shape<N, C>::kNodeIters], T *__restrict__ rhs)
+                                 const T (&mJ)[Shape<N, C>::kNodeIters], const T *__restrict__ q,
+                                 const Rotation<T> &rot, T *__restrict__ rhs)
 {
     constexpr int NODES = Shape<N, C>::kNodes;
 #pragma unroll
@@ -593,23 +616,28 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
             const int64_t g = B.g0 + t;
+            T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f) {
                 const T s = lds[f * NODES + t] + lds[(5 + f) * NODES + t] + lds[(10 + f) * NODES + t];
-                rhs[f * fstride + g] = s * mJ[it];
+                r[f] = s * mJ[it];
             }
+            if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
+#pragma unroll
+            for (int f = 0; f < 5; ++f) rhs[f * fstride + g] = r[f];
         }
     }
 }
 
 // One workgroup per batch of EPB elements.  SURF adds the entropy-conservative
-// surface term (face neighbours from nbr), giving the whole right-hand side.
+// surface term (face neighbours from nbr), giving the whole right-hand side;
+// rot.on adds the Coriolis source.
 template <typename T, int N, class C, bool SURF = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
 __attribute__((amdgpu_waves_per_eu(C::WAVES > 0 ? C::WAVES : 1)))
 volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
-                  const T *__restrict__ D, const int32_t *__restrict__ nbr, int64_t nelem,
-                  T *__restrict__ rhs)
+                  const T *__restrict__ D, const int32_t *__restrict__ nbr, Rotation<T> rot,
+                  int64_t nelem, T *__restrict__ rhs)
 {
     using S = Shape<N, C>;
     constexpr int Nq = N + 1;
@@ -618,6 +646,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     const Batch<N, C> B(blockIdx.x, nelem);
     const LineTask<N, C> L;
     const bool active = L.active(B.nvalid);
+    if constexpr (!SURF) rot.on = false;  // the volume term alone has no source
 
     // phase A: issue every global load first
     FaceLoads<T> face;
@@ -660,9 +689,9 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     write_partials<T, N, C>(lds, L, active, acc);
     __syncthreads();
     if constexpr (C::kFinalizeInLine) {
-        finish_line<T, N, C>(lds, L, active, B, fstride, acc, rhs);
+        finish_line<T, N, C>(lds, L, active, B, fstride, acc, q, rot, rhs);
     } else {
-        store_rhs<T, N, C>(lds, B, fstride, mJ, rhs);
+        store_rhs<T, N, C>(lds, B, fstride, mJ, q, rot, rhs);
     }
 }
 

@@ -60,7 +60,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("esdg_rhs_f64", "esdg_rhs_f32"):
         fn = getattr(lib, name)
         fn.restype = ci
-        fn.argtypes = [vp, vp, vp, vp, vp, ci, i64, vp, vp]
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64, vp, vp]
     lib.esdg_status_string.restype = ctypes.c_char_p
     lib.esdg_status_string.argtypes = [ci]
     lib.esdg_min_order.restype = ci
@@ -83,14 +83,27 @@ def esdg_volume_rhs_f32(q: int, phi: int, geom: int, D: int, N: int, nelem: int,
     return load().esdg_volume_rhs_f32(q, phi, geom, D, N, nelem, rhs, stream)
 
 
-def esdg_rhs_f64(q: int, phi: int, geom: int, D: int, nbr: int, N: int, nelem: int, rhs: int,
-                 stream: int = 0) -> int:
-    return load().esdg_rhs_f64(q, phi, geom, D, nbr, N, nelem, rhs, stream)
+def _host_vec3(omega, ctype):
+    """omega as a host array of 3 values (or None -> NULL)."""
+    if omega is None:
+        return None
+    vals = [float(x) for x in omega]
+    if len(vals) != 3:
+        raise ValueError("omega must have 3 components")
+    return (ctype * 3)(*vals)
 
 
-def esdg_rhs_f32(q: int, phi: int, geom: int, D: int, nbr: int, N: int, nelem: int, rhs: int,
-                 stream: int = 0) -> int:
-    return load().esdg_rhs_f32(q, phi, geom, D, nbr, N, nelem, rhs, stream)
+def esdg_rhs_f64(q: int, phi: int, geom: int, D: int, nbr: int, omega, N: int, nelem: int,
+                 rhs: int, stream: int = 0) -> int:
+    """omega: None or 3 numbers (host values)."""
+    return load().esdg_rhs_f64(q, phi, geom, D, nbr, _host_vec3(omega, ctypes.c_double), N, nelem,
+                               rhs, stream)
+
+
+def esdg_rhs_f32(q: int, phi: int, geom: int, D: int, nbr: int, omega, N: int, nelem: int,
+                 rhs: int, stream: int = 0) -> int:
+    return load().esdg_rhs_f32(q, phi, geom, D, nbr, _host_vec3(omega, ctypes.c_float), N, nelem,
+                               rhs, stream)
 
 
 def esdg_status_string(status: int) -> str:
@@ -116,18 +129,19 @@ def volume_rhs(q, phi, geom, D, out=None, stream=None):
     return _call(q, phi, geom, D, None, out, stream)
 
 
-def rhs(q, phi, geom, D, nbr, out=None, stream=None):
-    """rhs[5][nelem][Np] = volume + entropy-conservative surface term on the
-    GPU; nbr [nelem][6] int32 face neighbours on the same GPU (-1 = slip wall),
+def rhs(q, phi, geom, D, nbr, omega=None, out=None, stream=None):
+    """rhs[5][nelem][Np] = volume + entropy-conservative surface term (+ the
+    Coriolis source -omega x U when omega, 3 numbers, is given) on the GPU;
+    nbr [nelem][6] int32 face neighbours on the same GPU (-1 = slip wall),
     the rest as volume_rhs."""
     import torch
 
     if nbr is None or nbr.dtype != torch.int32:
         raise TypeError("nbr must be an int32 tensor")
-    return _call(q, phi, geom, D, nbr, out, stream)
+    return _call(q, phi, geom, D, nbr, out, stream, omega)
 
 
-def _call(q, phi, geom, D, nbr, out, stream):
+def _call(q, phi, geom, D, nbr, out, stream, omega=None):
     import torch
 
     dtype = q.dtype
@@ -176,7 +190,7 @@ def _call(q, phi, geom, D, nbr, out, stream):
         else:
             fn = esdg_rhs_f64 if dtype == torch.float64 else esdg_rhs_f32
             st = fn(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), nbr.data_ptr(),
-                    N, nelem, out.data_ptr(), handle)
+                    omega, N, nelem, out.data_ptr(), handle)
     if st != ESDG_OK:
         raise EsdgError(st, esdg_status_string(st))
     return out

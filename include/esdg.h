@@ -70,7 +70,7 @@ int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom,
 
 /*
  * Whole semi-discrete right-hand side of Eq. 2 of the same page (its volume
- * term plus its surface term, source h = 0), with the entropy-conservative
+ * term, its surface term and the source h), with the entropy-conservative
  * two-point flux also on the faces: the face dissipation the page adds to it
  * ([ESDG-GPU §3], from its reference [56]) is not part of this call.  At a
  * node on the xi_k = +-1 face of an element the surface term is
@@ -78,6 +78,10 @@ int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom,
  * w_end = 2/(N(N+1)) the LGL end weight, F* the same two-point flux as in
  * the volume (gravity term included).
  *
+ *   omega  HOST pointer to 3 values (read during the call, not kept), or NULL:
+ *        the rotation vector of the Coriolis term of Eq. 1b; the source is
+ *        h = -omega x U on the momentum (U = rho u), added at every node;
+ *        NULL means h = 0.  For a planet rotating at Omega, omega = 2 Omega.
  *   nbr  [nelem][6] int32, device: the element across each face, faces in the
  *        order -xi1, +xi1, -xi2, +xi2, -xi3, +xi3.  A neighbour index e' in
  *        [0, nelem) means the faces are conforming with the same orientation:
@@ -94,13 +98,13 @@ int esdg_volume_rhs_f32(const float *q, const float *phi, const float *geom,
  * overlap nbr either (ESDG_ERR_ALIAS), and nbr == NULL gives ESDG_ERR_NULL.
  */
 int esdg_rhs_f64(const double *q, const double *phi, const double *geom,
-                 const double *D, const int32_t *nbr, int N, int64_t nelem,
-                 double *rhs, hipStream_t stream);
+                 const double *D, const int32_t *nbr, const double *omega, int N,
+                 int64_t nelem, double *rhs, hipStream_t stream);
 
-/* The same in fp32 arithmetic. */
+/* The same in fp32 arithmetic (omega as 3 floats). */
 int esdg_rhs_f32(const float *q, const float *phi, const float *geom,
-                 const float *D, const int32_t *nbr, int N, int64_t nelem,
-                 float *rhs, hipStream_t stream);
+                 const float *D, const int32_t *nbr, const float *omega, int N,
+                 int64_t nelem, float *rhs, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *esdg_status_string(int status);

@@ -108,19 +108,23 @@ def test_alias_errors(fn, size):
 @pytest.mark.parametrize("fn,size", [(esdg.esdg_rhs_f64, 8), (esdg.esdg_rhs_f32, 4)])
 def test_rhs_argument_errors(fn, size):
     NB = 0x60000000
-    assert fn(A, B, C, Dp, NB, 0, 1, R, 0) == esdg.ESDG_ERR_ORDER
-    assert fn(A, B, C, Dp, NB, 4, -1, R, 0) == esdg.ESDG_ERR_NELEM
-    assert fn(0, 0, 0, 0, 0, 4, 0, 0, 0) == esdg.ESDG_OK
-    for i in range(6):
-        args = [A, B, C, Dp, NB, R]
-        args[i] = 0
-        assert fn(args[0], args[1], args[2], args[3], args[4], 4, 10, args[5], 0) == esdg.ESDG_ERR_NULL
+    om = (0.0, 0.0, 1e-4)
+    for w in (None, om):   # omega is optional (host values), checked after the pointers
+        assert fn(A, B, C, Dp, NB, w, 0, 1, R, 0) == esdg.ESDG_ERR_ORDER
+        assert fn(A, B, C, Dp, NB, w, 4, -1, R, 0) == esdg.ESDG_ERR_NELEM
+        assert fn(0, 0, 0, 0, 0, w, 4, 0, 0, 0) == esdg.ESDG_OK
+        for i in range(6):
+            args = [A, B, C, Dp, NB, R]
+            args[i] = 0
+            assert fn(args[0], args[1], args[2], args[3], args[4], w, 4, 10, args[5], 0) == esdg.ESDG_ERR_NULL
     # rhs overlapping the connectivity array
     N, nelem = 3, 100
-    assert fn(A, B, C, Dp, NB, N, nelem, NB + 6 * nelem * 4 - size, 0) == esdg.ESDG_ERR_ALIAS
-    assert fn(A, B, C, Dp, NB, N, nelem, NB - 5 * nelem * 64 * size + size, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, NB, None, N, nelem, NB + 6 * nelem * 4 - size, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, NB, om, N, nelem, NB - 5 * nelem * 64 * size + size, 0) == esdg.ESDG_ERR_ALIAS
     # and the inputs, as for the volume term
-    assert fn(A, B, C, Dp, NB, N, nelem, A + 4 * nelem * 64 * size, 0) == esdg.ESDG_ERR_ALIAS
+    assert fn(A, B, C, Dp, NB, None, N, nelem, A + 4 * nelem * 64 * size, 0) == esdg.ESDG_ERR_ALIAS
+    with pytest.raises(ValueError):
+        fn(A, B, C, Dp, NB, (1.0, 2.0), N, nelem, R, 0)
 
 
 def test_tensor_wrapper_rejects_cpu_tensors():

@@ -24,10 +24,10 @@ pytestmark = pytest.mark.gpu
 TOL = {np.float64: 1e-11, np.float32: 2e-5}
 
 
-def gpu_full_rhs(q, phi, geom, D, nbr):
+def gpu_full_rhs(q, phi, geom, D, nbr, omega=None):
     tq, tp, tg, tD = to_gpu(q, phi, geom, D)
     tn = torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev())
-    out = esdg.rhs(tq, tp, tg, tD, tn)
+    out = esdg.rhs(tq, tp, tg, tD, tn, omega=omega)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -188,3 +188,21 @@ def test_volume_entry_unchanged_by_surface_build():
     ref = oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)
     for f in range(5):
         assert np.abs(vol[f] - ref[f]).max() <= 1e-11 * np.abs(ref[f]).max()
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_coriolis_source(dtype):
+    """The baroclinic channel on an f-plane (omega = (0, 0, 2 * 7.292e-5 * sin 45 deg))
+    and a random state under a tilted rotation vector, against the oracle."""
+    wl = I.make("baroclinic")
+    f = 2 * 7.292e-5 * np.sin(np.pi / 4)
+    for om, (q, phi, geom, D, nbr, N) in (
+            ((0.0, 0.0, f), (wl.q, wl.phi, wl.geom, wl.D, wl.nbr, wl.N)),
+            ((3e-5, -1e-4, 1.2e-4), random_closed_mesh(5, (2, 3, 2), (True, False, True), seed=77)[:5] + (5,))):
+        q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+        om_t = tuple(float(np.asarray(x, dtype=dtype)) for x in om)   # what the kernel sees
+        got = gpu_full_rhs(q, phi, geom, D, nbr, omega=om_t)
+        ref, mag = oracle.rhs(q, phi, geom, D, nbr, N, omega=np.array(om_t), with_magnitude=True)
+        check_full(got, ref, mag, TOL[dtype], f"Coriolis omega={om} {np.dtype(dtype).name}")
+        base = gpu_full_rhs(q, phi, geom, D, nbr)
+        assert np.array_equal(got[0], base[0]) and np.array_equal(got[4], base[4])
