@@ -279,6 +279,22 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     acc_l[4] = fma(Dla, FE, acc_l[4]);
 }
 
+// XCD-aware order of the batches.  The hardware hands workgroup i to
+// accelerator die (XCD) i mod kXcds, each with its own L2; this permutation
+// gives every XCD one contiguous range of batches instead, so elements that
+// are neighbours in the mesh order run on the same die at about the same
+// time and the surface term's face partners come from that die's L2.  It is
+// a bijection of [0, nb) for any nb, so results do not depend on the real
+// dispatch order.
+constexpr int kXcds = 8;
+
+__device__ inline int64_t xcd_batch(int64_t block, int64_t nb)
+{
+    const int64_t x = block % kXcds, i = block / kXcds;
+    const int64_t q = nb / kXcds, r = nb % kXcds;
+    return x * q + (x < r ? x : r) + i;
+}
+
 // Per-thread view of one workgroup's batch of elements.
 template <int N, class C>
 struct Batch {
@@ -643,7 +659,9 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     constexpr int Nq = N + 1;
     __shared__ T lds[S::kLdsValues];
     const int64_t fstride = nelem * S::Np;
-    const Batch<N, C> B(blockIdx.x, nelem);
+    // the whole right-hand side walks the batches in XCD-contiguous order
+    const int64_t batch = SURF ? xcd_batch(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+    const Batch<N, C> B(batch, nelem);
     const LineTask<N, C> L;
     const bool active = L.active(B.nvalid);
     if constexpr (!SURF) rot.on = false;  // the volume term alone has no source
@@ -651,7 +669,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     // phase A: issue every global load first
     FaceLoads<T> face;
     if constexpr (SURF) {
-        if (active) face.issue_neighbours(nbr, (int64_t)blockIdx.x * C::EPB + L.eb, L.k);
+        if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
     }
     NodeLoads<T, N, C> ld;
     ld.issue(q, phi, geom, fstride, B);

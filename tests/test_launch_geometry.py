@@ -190,3 +190,20 @@ def test_face_partner_indices(dtype, N, K, periodic):
                 assert pa[k] == N - abc(own)[k]
                 assert [x for i, x in enumerate(pa) if i != k] == tang
     assert np.all(seen == 1)
+
+
+def test_xcd_batch_order_is_a_bijection():
+    """The whole right-hand side maps workgroup b to batch xcd_batch(b, nb):
+    every batch is taken exactly once, for any grid size."""
+    text = open(KERNEL).read()
+    assert "const int64_t x = block % kXcds, i = block / kXcds;" in text
+    assert "return x * q + (x < r ? x : r) + i;" in text
+    X = int(re.search(r"constexpr int kXcds = (\d+);", text).group(1))
+
+    def xcd_batch(block, nb):
+        x, i = block % X, block // X
+        q, r = nb // X, nb % X
+        return x * q + (x if x < r else r) + i
+
+    for nb in list(range(1, 200)) + [1366, 3414, 4609, 87382]:
+        assert sorted(xcd_batch(b, nb) for b in range(nb)) == list(range(nb))
