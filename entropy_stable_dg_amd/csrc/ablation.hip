@@ -167,9 +167,16 @@ __device__ inline void stage(const double *__restrict__ q, const double *__restr
         lds[pW * G::Np + t] = ph - 0.5 * usq;
         lds[pIB * G::Np + t] = 1.0 / bs;
     }
+    if (variant >= CONTRA) {
+        // the production pair routine takes u/2, w/2 and phi/4
+        for (int m = 0; m < 3; ++m) lds[(pU + m) * G::Np + t] *= 0.5;
+        lds[pW * G::Np + t] *= 0.5;
+        lds[pPhi * G::Np + t] *= 0.25;
+    }
 }
 
-// NodeRegs of the production pair math, read from the primitive layout.
+// NodeRegs of the production pair math, read from the primitive layout (for
+// these rungs u, w and phi are staged as u/2, w/2 and phi/4).
 template <int N>
 __device__ inline NodeRegs<double> node_regs(const double *lds, int s, int k)
 {

@@ -133,7 +133,10 @@ __device__ inline float select(bool c, float a, float b)
 }
 
 // Values staged per node in LDS (field-major: value v of node t at v*NODES+t).
-// kW holds w = phi - |u|^2/2 (the energy flux needs only the pair mean of w).
+// Scaled where the pair only needs a pair mean or a jump, so the pair does
+// not multiply by constants: kU1..kU3 hold u/2 (X.u + Y.u = {{u}}), kW holds
+// w/2 with w = phi - |u|^2/2 (the energy flux needs {{w}} only), kPhi holds
+// phi/4 (the gravity term needs (1/4) [[phi]] only).
 // The three metric values Ja^k_1..3 of a node sit at kJa + 3k.
 enum NodeValue {
     kRho = 0, kU1, kU2, kU3, kB, kLogRho, kLogB, kPhi, kW, kInvB, kJa,
@@ -247,22 +250,22 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     const T iLb = select(ser_b, pb * isb, lnk * (Y.lb - X.lb) * iBb);
     // {{rho}}/(2{{b}}) with the b scaling undone
     const T pt = half_bscale * sr * isb;
-    // metric of the pair: Ja^k(a) + Ja^k(l)
+    // metric of the pair: Ja^k(a) + Ja^k(l); {{u}} (staged u is halved)
     const T c1 = X.n1 + Y.n1, c2 = X.n2 + Y.n2, c3 = X.n3 + Y.n3;
     const T s1 = X.u1 + Y.u1, s2 = X.u2 + Y.u2, s3 = X.u3 + Y.u3;
     // contravariant density flux {{rho}}_log ({{u}} . c)
-    const T Fr = T(0.5) * Lr * (c1 * s1 + c2 * s2 + c3 * s3);
-    const T hF = T(0.5) * Fr;
+    const T Fr = Lr * (c1 * s1 + c2 * s2 + c3 * s3);
     // symmetric momentum part S~_m = F~rho {{u_m}} + c_m {{rho}}/(2{{b}})
-    const T S1 = fma(hF, s1, c1 * pt);
-    const T S2 = fma(hF, s2, c2 * pt);
-    const T S3 = fma(hF, s3, c3 * pt);
+    const T S1 = fma(Fr, s1, c1 * pt);
+    const T S2 = fma(Fr, s2, c2 * pt);
+    const T S3 = fma(Fr, s3, c3 * pt);
     // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~,
-    // with -{{|u|^2}}/2 + {{phi}} = {{w}}
-    const T coef = fma(cE, iLb, T(0.5) * (X.w + Y.w));
-    const T FE = fma(coef, Fr, T(0.5) * (s1 * S1 + s2 * S2 + s3 * S3));
+    // with -{{|u|^2}}/2 + {{phi}} = {{w}} (staged w is halved)
+    const T coef = fma(cE, iLb, X.w + Y.w);
+    const T FE = fma(coef, Fr, s1 * S1 + s2 * S2 + s3 * S3);
     // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
-    const T g = T(0.25) * sb * Lr * (Y.ph - X.ph);
+    // = (s_b b_a + s_b b_l) {{rho}}_log [[phi/4]] / (s_b b_own)  (staged phi is phi/4)
+    const T g = sb * Lr * (Y.ph - X.ph);
     const T ga = g * X.ib;
     const T gl = -g * Y.ib;
     const T Dal = *Dal_p;
@@ -382,18 +385,19 @@ __device__ inline NodeRegs<T> node_values(T rho, T m1, T m2, T m3, T E, T ph)
     const T bscale = T(kBScale);
     NodeRegs<T> V;
     const T irho = A::rcp(rho);
+    const T hirho = T(0.5) * irho;
     V.rho = rho;
-    V.u1 = m1 * irho;
-    V.u2 = m2 * irho;
-    V.u3 = m3 * irho;
-    const T usq = V.u1 * V.u1 + V.u2 * V.u2 + V.u3 * V.u3;
-    const T p = gm1 * (E - T(0.5) * (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - rho * ph);
+    V.u1 = m1 * hirho;                                  // u/2
+    V.u2 = m2 * hirho;
+    V.u3 = m3 * hirho;
+    const T usq4 = V.u1 * V.u1 + V.u2 * V.u2 + V.u3 * V.u3;  // |u|^2 / 4
+    const T p = gm1 * (E - (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - rho * ph);
     V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
     V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
     V.lrho = A::node_log(rho);
     V.lb = A::node_log(V.b);
-    V.ph = ph;
-    V.w = ph - T(0.5) * usq;
+    V.ph = T(0.25) * ph;                          // phi/4
+    V.w = fma(T(0.5), ph, -usq4);                 // w/2 = (phi - |u|^2/2)/2
     return V;
 }
 
