@@ -58,3 +58,27 @@ def test_variant_rejected():
     tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
     with pytest.raises(Exception, match="status -6"):
         abl.volume_rhs(abl.ESDG_ABL_COUNT, tq, tp, tg, tD)
+
+
+def test_ladder_at_the_timed_size():
+    """The configuration bench.py times the ladder on: the bubble workload
+    tiled 64 times (N = 4, 262,144 elements).  The kernels are element-local
+    and free of atomics, so every tile must reproduce the single bubble's
+    result bitwise; the single bubble is checked against the oracle in
+    test_variant_bubble.  A sample of tiles (first, middle, last) is compared."""
+    wl = I.make("bubble")
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    reps = 64
+    big = (tq.repeat(1, reps, 1), tp.repeat(reps, 1), tg.repeat(1, reps, 1))
+    ne = wl.nelem
+    for variant in [abl.ESDG_ABL_BASELINE, abl.ESDG_ABL_CONTRA, abl.ESDG_ABL_SYM_UPPER,
+                    abl.ESDG_ABL_SYM_WEIGHTED | abl.ESDG_ABL_FUSE_FLAG, abl.ESDG_ABL_FUSED]:
+        print(f"[ablation] variant {variant:#x} at 262,144 elements", flush=True)
+        small = abl.volume_rhs(variant, tq, tp, tg, tD)
+        out = abl.volume_rhs(variant, big[0], big[1], big[2], tD)
+        torch.cuda.synchronize()
+        for t in (0, reps // 2, reps - 1):
+            assert torch.equal(out[:, t * ne:(t + 1) * ne], small), (variant, t)
+        del out
+    del big
+    torch.cuda.empty_cache()
