@@ -35,10 +35,18 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and blank lines removed, so
+    editing a comment does not orphan the counters taken on the same code)."""
+    import re
+
     h = hashlib.sha256()
     for rel in SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

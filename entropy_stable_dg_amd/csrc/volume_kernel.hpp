@@ -22,7 +22,9 @@
 //   * Phase A, one thread per node: coalesced SoA loads of the 5 conserved
 //     fields and phi; primitives, p, the scaled b = s_b rho/(2p), the logs
 //     of rho and b and 1/b are computed once per node and staged in LDS.
-//   * Phase A also stages the metric terms Ja^k_j (coalesced loads).
+//     The metric terms Ja^k_j are either staged in LDS too or loaded by each
+//     line thread for its own line straight into registers (a per-order
+//     launch choice).
 //   * Phase B, one thread per grid line (3 Nq^2 lines per element): every
 //     unordered pair (a, l) of the line is evaluated once, with both nodes'
 //     values read from LDS where the pair needs them:
@@ -34,7 +36,15 @@
 //     direction, every slot written by exactly one thread: no atomics, the
 //     result is bitwise reproducible).
 //   * Phase D, one thread per node: sum of the three directional partials,
-//     scaling by -1/J, coalesced SoA store.
+//     scaling by -1/J, coalesced SoA store (or, with FIN, the direction-3
+//     line threads finish their own nodes).
+//
+// The whole right-hand side (SURF) reuses this kernel: a line's two end
+// nodes lie on the element's two xi_k faces, so the line thread adds the
+// entropy-conservative face flux with each end's partner in the neighbouring
+// element (or the mirror state at a slip wall) to that end's accumulator
+// ([ESDG-GPU §3, Eq. 2], surface part); the Coriolis source of Eq. 1b is
+// added at the store.
 #pragma once
 
 #include <hip/hip_runtime.h>
