@@ -212,6 +212,76 @@ def time_ablation(steps: int, warmup: int) -> dict:
             "production": {"ms": prod, "speedup_vs_baseline": base / prod, "dof_per_s": dof / (prod * 1e-3)}}
 
 
+def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"),
+                   steps: int = 20) -> dict:
+    """Throughput of the volume term at every order N and refinement level L
+    (N_e = 2^(3L) elements, one base element as in the page's Fig. 3 and
+    Fig. 5): the bubble-shaped state on a warped 8^3 mesh (L = 3) is built on
+    the host once per order and tiled on the GPU to reach L = 4..6 (the kernel
+    is element-local, so tiling leaves the work and traffic per element
+    unchanged).  Below 512 MB of footprint, launches rotate over enough copies
+    that inputs are not cache-resident."""
+    import torch
+
+    from entropy_stable_dg_amd import esdg, inputs, perfmodel
+
+    dev = torch.device("cuda:0")
+    handle = torch.cuda.current_stream(dev).cuda_stream
+    points = []
+    for dtype in dtypes:
+        fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
+        for N in orders:
+            wl = inputs.build_workload(f"sweep_N{N}", (8, 8, 8), (0, 0, 0), (1000, 1000, 1000), N,
+                                       "bubble", seed=600 + N, warp_frac=0.05, dtype=dtype,
+                                       periodic=(True, True, False))
+            base = [torch.from_numpy(a).to(dev) for a in (wl.q, wl.phi, wl.geom, wl.D)]
+            for L in levels:
+                reps = 8 ** (L - 3)
+                q = base[0].repeat(1, reps, 1)
+                phi = base[1].repeat(reps, 1)
+                geom = base[2].repeat(1, reps, 1)
+                D = base[3]
+                nelem = q.shape[1]
+                footprint = (q.numel() * 2 + phi.numel() + geom.numel()) * q.element_size()
+                nsets = max(1, math.ceil(512e6 / footprint)) if footprint < 512e6 else 1
+                sets = [(q, phi, geom, torch.empty_like(q))]
+                for _ in range(nsets - 1):
+                    sets.append((q.clone(), phi.clone(), geom.clone(), torch.empty_like(q)))
+                ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), r.data_ptr()) for a, b, c, r in sets]
+
+                def run(k: int) -> None:
+                    for i in range(k):
+                        p = ptrs[i % nsets]
+                        if fn(p[0], p[1], p[2], D.data_ptr(), N, nelem, p[3], handle) != 0:
+                            raise RuntimeError("volume term launch failed")
+
+                run(3)
+                torch.cuda.synchronize()
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                run(steps)
+                t1.record()
+                torch.cuda.synchronize()
+                sec = t0.elapsed_time(t1) * 1e-3 / steps
+                dof = nelem * (N + 1) ** 3
+                flops = perfmodel.flops_per_element(N) * nelem
+                nbytes = perfmodel.algorithmic_bytes(N, nelem, dtype)
+                pt = {"dtype": dtype, "N": N, "L": L, "nelem": nelem, "dof": dof, "us": sec * 1e6,
+                      "gdof_s": dof / sec / 1e9, "analytic_tflops": flops / sec / 1e12,
+                      "hbm_gbs": nbytes / sec / 1e9,
+                      "arithmetic_intensity": perfmodel.arithmetic_intensity(N, dtype)}
+                if dtype == "f64":
+                    pt["frac_fp64_vector_peak"] = pt["analytic_tflops"] / perfmodel.PEAK_FP64_VECTOR_TFLOPS
+                points.append(pt)
+                log(f"sweep {dtype} N={N} L={L}: {nelem} el., {pt['us']:.1f} us, {pt['gdof_s']:.2f} GDOF/s, "
+                    f"{pt['analytic_tflops']:.2f} TF/s, {pt['hbm_gbs']:.0f} GB/s")
+                del sets, q, phi, geom
+                torch.cuda.empty_cache()
+            del base
+    return {"sweep": "volume term, every order and refinement level (N_e = 2^(3L))",
+            "steps": steps, "points": points}
+
+
 def cpu_one_core(wl, seconds: float) -> dict:
     """The oracle on one host thread over a bounded leading slice of the
     workload's elements (element-local work, so DOF/s carries over)."""
@@ -271,6 +341,9 @@ def main() -> int:
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
     ap.add_argument("--ablation-steps", type=int, default=10)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the all-orders roofline sweep (N = 1..8, L = 3..6, fp64 and fp32); "
+                         "prints its own JSON line")
     ap.add_argument("--all", action="store_true",
                     help="time every workload (tiny, baroclinic, bubble_f32, high_order) as extras")
     args = ap.parse_args()
@@ -292,6 +365,13 @@ def main() -> int:
     log(f"device: {torch.cuda.get_device_name(0)}; kernel source {kernel_source_hash()}")
     if args.profile_pass:
         print(json.dumps(profile_pass(args.steps, args.workload)), flush=True)
+        return 0
+    if args.sweep:
+        from entropy_stable_dg_amd import probe
+        out = roofline_sweep()
+        out["hbm_stream81_gbs"] = max(probe.stream81_bandwidth(), probe.stream81_bandwidth(wide=True))
+        out["kernel_source_hash"] = kernel_source_hash()
+        print(json.dumps(out), flush=True)
         return 0
 
     t_cold, t_hot, info, wl = time_workload(HEADLINE, args.steps, args.warmup, args.rotate_mb * 1e6)
