@@ -142,3 +142,20 @@ def test_tensor_wrapper_rejects_cpu_tensors():
         esdg.rhs(q, phi, geom, D, nbr)
     with pytest.raises(TypeError):
         esdg.rhs(q, phi, geom, D, nbr.long())
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: a binding pointed at a library that is not there raises."""
+    from entropy_stable_dg_amd import ablation
+    for mod in (esdg, probe, ablation):
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load(str(tmp_path / "not_built.so"))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
