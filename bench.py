@@ -79,9 +79,13 @@ def measured_counter(workload: str, dtype: str, field: str):
     return rec.get(field)
 
 
-def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False):
+def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False,
+                  graph: bool = False):
     """Returns (seconds per step rotating cold buffers, seconds per step hot, info).
-    With `full`, the whole right-hand side (volume + surface, esdg_rhs_*)."""
+    With `full`, the whole right-hand side (volume + surface, esdg_rhs_*).
+    With `graph`, the steps are captured once in a HIP graph (through torch's
+    graph API) and the graph is replayed: the same launches without the
+    per-launch host overhead."""
     import torch
 
     from entropy_stable_dg_amd import esdg, inputs, perfmodel
@@ -123,13 +127,39 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
     for rotate in (True, False):
         run(warmup, rotate)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        run(steps, rotate)
-        end.record(stream)
-        torch.cuda.synchronize()
-        results[rotate] = start.elapsed_time(end) * 1e-3 / steps
-        log(f"{name}: {'rotating' if rotate else 'hot'} {results[rotate] * 1e6:.2f} us/step")
+        if graph:
+            per_graph = min(steps, 100)
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                handle = side.cuda_stream
+                run(2, rotate)                      # warm-up on the capture stream
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                handle = side.cuda_stream
+                run(per_graph, rotate)
+            handle = stream.cuda_stream
+            replays = max(1, steps // per_graph)
+            g.replay()
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for _ in range(replays):
+                g.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            results[rotate] = start.elapsed_time(end) * 1e-3 / (replays * per_graph)
+            del g
+        else:
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            run(steps, rotate)
+            end.record(stream)
+            torch.cuda.synchronize()
+            results[rotate] = start.elapsed_time(end) * 1e-3 / steps
+        log(f"{name}{' (graph replay)' if graph else ''}: {'rotating' if rotate else 'hot'} {results[rotate] * 1e6:.2f} us/step")
     info = dict(N=N, nelem=nelem, dof=wl.dof, dtype=dtype, description=wl.description,
                 seed=wl.seed, buffer_sets=nsets,
                 bytes=perfmodel.algorithmic_bytes(N, nelem, dtype),
@@ -351,7 +381,8 @@ def main() -> int:
                          "high_order; a ':rhs' suffix profiles the whole right-hand side)")
     ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs",
                     help="comma-separated extra workloads to time (reported under 'extra'); "
-                         "a ':rhs' suffix times the whole right-hand side (volume + surface)")
+                         "a ':rhs' suffix times the whole right-hand side (volume + surface), "
+                         "':graph' replays the launches from a captured HIP graph")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
     ap.add_argument("--ablation-steps", type=int, default=10)
@@ -398,12 +429,13 @@ def main() -> int:
     extra = {}
     names = [x for x in args.extra.split(",") if x]
     if args.all:
-        names = ["tiny", "baroclinic", "bubble_f32", "high_order", "bubble:rhs", "bubble_f32:rhs",
-                 "baroclinic:rhs", "high_order:rhs"]
+        names = ["tiny", "tiny:graph", "baroclinic", "bubble_f32", "high_order", "bubble:rhs",
+                 "bubble_f32:rhs", "baroclinic:rhs", "high_order:rhs"]
     for key in names:
         name, _, mode = key.partition(":")
         full = mode == "rhs"
-        c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6, full=full)
+        c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6, full=full,
+                                     graph=(mode == "graph"))
         extra[key] = {
             "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
@@ -415,6 +447,8 @@ def main() -> int:
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                       if inf["dtype"] == "f64" else None),
         }
+        if mode == "graph":
+            extra[key]["what"] = "the same launches captured once in a HIP graph and replayed"
         if full:
             extra[key]["hbm_gbs_with_face_partners"] = inf["bytes_with_face_partners"] / c / 1e9
             extra[key]["what"] = "whole right-hand side: volume + entropy-conservative surface term"
