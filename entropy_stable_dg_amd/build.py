@@ -59,7 +59,9 @@ def build(verbose: bool = False) -> str:
 
 def is_stale() -> bool:
     """True when the library is missing or older than one of its sources."""
-    for lib, deps in ((LIB, DEPENDS), (PROBE_LIB, PROBE_SOURCES), (ABLATION_LIB, ABLATION_DEPENDS)):
+    probe_deps = PROBE_SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"),
+                                  os.path.join(INCLUDE, "esdg_probe.h")]
+    for lib, deps in ((LIB, DEPENDS), (PROBE_LIB, probe_deps), (ABLATION_LIB, ABLATION_DEPENDS)):
         if not os.path.exists(lib):
             return True
         t = os.path.getmtime(lib)

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "esdg_probe.h"
+#include "volume_kernel.hpp"
 
 namespace {
 
@@ -61,6 +62,19 @@ copy(const double *__restrict__ src, double *__restrict__ dst, int64_t n)
         dst[i] = src[i];
 }
 
+// The per-node natural log of the volume kernel, element by element (a test
+// hook for its accuracy: the fp64 form is the library's own series, the fp32
+// form the hardware log2 scaled by ln 2, exactly as the pairs use them).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+node_log(const T *__restrict__ x, T *__restrict__ y, int64_t n)
+{
+    using A = esdg::Arith<T>;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+        y[i] = T(A::kLogToLn) * A::node_log(x[i]);
+}
+
 unsigned grid_for(int64_t n)
 {
     int dev = 0, cus = 256;
@@ -99,6 +113,22 @@ int esdg_probe_stream81_wide_f64(const double *src, double *dst, int64_t n, hipS
     if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0 || n % 2 != 0) return -2;
     hipLaunchKernelGGL(stream81_wide, dim3(grid_for((n + 3) / 4)), dim3(kThreads), 0, stream, src,
                        dst, n);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int esdg_probe_node_log_f64(const double *x, double *y, int64_t n, hipStream_t stream)
+{
+    const int st = check(x, y, n, 2);
+    if (st || n == 0) return st;
+    hipLaunchKernelGGL(node_log<double>, dim3(grid_for(n)), dim3(kThreads), 0, stream, x, y, n);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int esdg_probe_node_log_f32(const float *x, float *y, int64_t n, hipStream_t stream)
+{
+    const int st = check(x, y, n, 1);
+    if (st || n == 0) return st;
+    hipLaunchKernelGGL(node_log<float>, dim3(grid_for(n)), dim3(kThreads), 0, stream, x, y, n);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -7,7 +7,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_LIB_PATH = os.path.join(HERE, "libesdg_probe.so")
-EXPORTS = ("esdg_probe_stream81_f64", "esdg_probe_stream81_wide_f64", "esdg_probe_copy_f64")
+EXPORTS = ("esdg_probe_stream81_f64", "esdg_probe_stream81_wide_f64", "esdg_probe_node_log_f64",
+           "esdg_probe_node_log_f32", "esdg_probe_copy_f64")
 
 _lib = None
 
@@ -38,6 +39,14 @@ def esdg_probe_stream81_f64(src: int, dst: int, n: int, stream: int = 0) -> int:
 
 def esdg_probe_stream81_wide_f64(src: int, dst: int, n: int, stream: int = 0) -> int:
     return load().esdg_probe_stream81_wide_f64(src, dst, n, stream)
+
+
+def esdg_probe_node_log_f64(x: int, y: int, n: int, stream: int = 0) -> int:
+    return load().esdg_probe_node_log_f64(x, y, n, stream)
+
+
+def esdg_probe_node_log_f32(x: int, y: int, n: int, stream: int = 0) -> int:
+    return load().esdg_probe_node_log_f32(x, y, n, stream)
 
 
 def esdg_probe_copy_f64(src: int, dst: int, n: int, stream: int = 0) -> int:

@@ -3,6 +3,9 @@
  * measure the bandwidth roof on the device the volume kernel runs on.  Not
  * part of the volume-term path; the benchmark and the profiling runs use it.
  *
+ * The node-log entries expose the volume kernel's per-node logarithm for
+ * accuracy tests.
+ *
  * The 8-read:1-write fp64 stream is the empirical streaming roofline of
  * "hipBone: A performance-portable GPU-accelerated C++ version of the
  * NekBone benchmark" (its bandwidth section: a kernel reading eight arrays
@@ -32,6 +35,12 @@ int esdg_probe_stream81_f64(const double *src, double *dst, int64_t n, hipStream
 /* The same stream with 32 bytes per lane per array (16-byte loads); src and
  * dst 16-byte aligned and n even, else -2. */
 int esdg_probe_stream81_wide_f64(const double *src, double *dst, int64_t n, hipStream_t stream);
+
+/* y[i] = natural log of x[i] as the volume kernel computes its per-node logs
+ * (fp64: the library's own series; fp32: hardware log2 times ln 2), i < n.
+ * A test hook for the accuracy of that log; x must be positive and normal. */
+int esdg_probe_node_log_f64(const double *x, double *y, int64_t n, hipStream_t stream);
+int esdg_probe_node_log_f32(const float *x, float *y, int64_t n, hipStream_t stream);
 
 /* dst[i] = src[i], i < n: reads and writes 8 n bytes. */
 int esdg_probe_copy_f64(const double *src, double *dst, int64_t n, hipStream_t stream);
