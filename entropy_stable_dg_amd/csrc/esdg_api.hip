@@ -15,27 +15,32 @@ constexpr int kMaxOrder = 8;
 
 // Launch shape per precision and order: EPB elements x NT threads per
 // workgroup (the 3 (N+1)^2 line tasks of EPB elements fill whole waves as far
-// as possible), and whether the metric terms are staged in LDS.  Chosen by
-// timing on MI355X at the bubble, baroclinic and N=4 L=6 mesh sizes.
+// as possible), whether the metric terms are staged in LDS, and whether the
+// pair loop carries its series-only second form (volume term / with the
+// surface term).  Chosen by timing on MI355X at the bubble, baroclinic and
+// N=4 L=6 mesh sizes; the series form where it measured faster at the
+// 4096- and 32,768-element sizes (it adds registers: at N <= 2 it gains
+// nothing, and the fp64 N = 8 kernel would spill).
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
-// registers, direction-major line order, direction-3 lines finish the nodes>
+// registers, direction-major line order, direction-3 lines finish the nodes,
+// series form (volume term), series form (with the surface term)>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
-template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false>; };              // 192/192
-template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true>; }; // 225/256
-template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128>; };                        // 108/128
-template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192>; };                        // 147/192
-template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true>; }; // 192/192
+template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true>; };          // 192/192
+template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
+template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128, 0, true, false, false, false, true, true>; };     // 108/128
+template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, false, false, true>; };          // 147/192
+template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256>; };                        // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
-template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192>; };
-template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true>; };
-template <> struct Launch<float, 5> { using C = LaunchCfg<1, 128, 0, false>; };
-template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false>; };
-template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false>; };
-template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false>; };
+template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, false, false, true, true>; };
+template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true>; };
+template <> struct Launch<float, 5> { using C = LaunchCfg<1, 128, 0, false, false, false, false, true>; };
+template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
+template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
+template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, false, false, true, true>; };
 
 template <typename T, int N, bool SURF>
 int launch(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,

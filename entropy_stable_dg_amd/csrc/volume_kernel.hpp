@@ -159,7 +159,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 // SIMD (it then caps the registers); METRIC_LDS stages the metric terms in
 // LDS (coalesced loads in phase A) instead of loading them per line thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
-          bool KMAJOR_ = false, bool FIN_ = false>
+          bool KMAJOR_ = false, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -175,6 +175,11 @@ struct LaunchCfg {
     // two other directions' partials from LDS, scaling by -1/J, storing), so
     // LDS holds two directional partials instead of three.
     static constexpr bool kFinalizeInLine = FIN_;
+    // SERIES: the pair loop has a second form for waves whose lines all take
+    // the series branch of the log means (fewer instructions per pair, more
+    // registers); SERIES_SURF the same for the kernel with the surface term.
+    static constexpr bool kSeriesForm = SERIES_;
+    static constexpr bool kSeriesFormSurf = SERIES_SURF_;
 };
 
 template <int N, class C>
@@ -217,12 +222,26 @@ struct NodeRegs {
     }
 };
 
+// Series branch of the log means in f = s^2, s = jump/sum of the two states:
+// s/atanh(s) = 1 - f/3 - 4f^2/45 - 44f^3/945 - ... (halved here) and
+// atanh(s)/s = 1 + f/3 + f^2/5 + f^3/7 + ... (doubled here).
+template <typename T>
+__device__ inline T half_s_over_atanh(T f)
+{
+    return fma(fma(fma(T(-22.0 / 945.0), f, T(-2.0 / 45.0)), f, T(-1.0 / 6.0)), f, T(0.5));
+}
+template <typename T>
+__device__ inline T two_atanh_over_s(T f)
+{
+    return fma(fma(fma(T(2.0 / 7.0), f, T(2.0 / 5.0)), f, T(2.0 / 3.0)), f, T(2));
+}
+
 // Contribution of the unordered pair (a, l) of one line, both directions of
 // the pair, added to the accumulators of nodes a and l.
 // X and Y are taken by value: a reference would take the address of the
 // caller's locals, and the compiler fence in the pair loop would then keep
 // them in scratch memory.  D[a][l] and D[l][a] are read where they are used.
-template <typename T>
+template <typename T, bool SERIES = false>
 __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
                                    const T *__restrict__ Dal_p, const T *__restrict__ Dla_p,
                                    T *acc_a, T *acc_l)
@@ -235,29 +254,39 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     // sums and jumps (jumps are partner l minus receiving node a)
     const T sr = X.rho + Y.rho, dr = Y.rho - X.rho;
     const T sb = X.b + Y.b, db = Y.b - X.b;
-    const bool ser_r = fabs(dr) < eps * sr;
-    const bool ser_b = fabs(db) < eps * sb;
-    // one reciprocal serves 1/sr, 1/sb, 1/(ln rho_l - ln rho_a), 1/db
-    const T Ar = select(ser_r, T(1), lnk * (Y.lrho - X.lrho));
-    const T Bb = select(ser_b, T(1), db);
-    const T srsb = sr * sb, AB = Ar * Bb;
-    const T R = A::rcp(srsb * AB);
-    const T isr = R * sb * AB;
-    const T isb = R * sr * AB;
-    const T iAr = R * srsb * Bb;
-    const T iBb = R * srsb * Ar;
-    // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference);
-    // s/atanh(s) = 1 - f/3 - 4f^2/45 - 44f^3/945 - ..., f = s^2, halved here
-    const T tr = dr * isr;
-    const T fr = tr * tr;
-    const T qr = fma(fma(fma(T(-22.0 / 945.0), fr, T(-2.0 / 45.0)), fr, T(-1.0 / 6.0)), fr, T(0.5));
-    const T Lr = select(ser_r, sr * qr, dr * iAr);
-    // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db;
-    // atanh(s)/s = 1 + f/3 + f^2/5 + f^3/7 + ..., doubled here
-    const T tb = db * isb;
-    const T fb = tb * tb;
-    const T pb = fma(fma(fma(T(2.0 / 7.0), fb, T(2.0 / 5.0)), fb, T(2.0 / 3.0)), fb, T(2));
-    const T iLb = select(ser_b, pb * isb, lnk * (Y.lb - X.lb) * iBb);
+    T Lr, iLb, isb;
+    if constexpr (SERIES) {
+        // The caller guarantees that both log means take their series form
+        // (every pair of the line is within the threshold).  The values are
+        // those of the general form below with its log-difference factors
+        // Ar = Bb = 1 (exact), so the result does not depend on the form.
+        const T srsb = sr * sb;
+        const T R = A::rcp(srsb);
+        const T isr = R * sb;
+        isb = R * sr;
+        const T tr = dr * isr;
+        Lr = sr * half_s_over_atanh(tr * tr);
+        const T tb = db * isb;
+        iLb = two_atanh_over_s(tb * tb) * isb;
+    } else {
+        const bool ser_r = fabs(dr) < eps * sr;
+        const bool ser_b = fabs(db) < eps * sb;
+        // one reciprocal serves 1/sr, 1/sb, 1/(ln rho_l - ln rho_a), 1/db
+        const T Ar = select(ser_r, T(1), lnk * (Y.lrho - X.lrho));
+        const T Bb = select(ser_b, T(1), db);
+        const T srsb = sr * sb, AB = Ar * Bb;
+        const T R = A::rcp(srsb * AB);
+        const T isr = R * sb * AB;
+        isb = R * sr * AB;
+        const T iAr = R * srsb * Bb;
+        const T iBb = R * srsb * Ar;
+        // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference)
+        const T tr = dr * isr;
+        Lr = select(ser_r, sr * half_s_over_atanh(tr * tr), dr * iAr);
+        // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
+        const T tb = db * isb;
+        iLb = select(ser_b, two_atanh_over_s(tb * tb) * isb, lnk * (Y.lb - X.lb) * iBb);
+    }
     // {{rho}}/(2{{b}}) with the b scaling undone
     const T pt = half_bscale * sr * isb;
     // metric of the pair: Ja^k(a) + Ja^k(l); {{u}} (staged u is halved)
@@ -525,11 +554,35 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
     }
 }
 
-// Phase B: every unordered pair of this thread's line.
+// True when every pair of this thread's line takes the series form of both
+// log means: any pair's jump is at most max - min along the line and its sum
+// at least 2 min, so (max - min) < 2 eps min implies the per-pair test; the
+// 1 % margin covers that test's rounding.  NaN states give false.
 template <typename T, int N, class C>
-__device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const LineTask<N, C> &L,
-                                  const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
-                                  T (&acc)[N + 1][5])
+__device__ inline bool line_in_series(const T *lds, const LineTask<N, C> &L)
+{
+    constexpr int NODES = Shape<N, C>::kNodes;
+    T rmin = lds[kRho * NODES + L.nb], rmax = rmin;
+    T bmin = lds[kB * NODES + L.nb], bmax = bmin;
+#pragma unroll
+    for (int a = 1; a < N + 1; ++a) {
+        const T r = lds[kRho * NODES + L.nb + a * L.step];
+        const T b = lds[kB * NODES + L.nb + a * L.step];
+        rmin = fmin(rmin, r);
+        rmax = fmax(rmax, r);
+        bmin = fmin(bmin, b);
+        bmax = fmax(bmax, b);
+    }
+    const T lim = T(0.99 * 2.0 * Arith<T>::kSeries);
+    return (rmax - rmin) < lim * rmin && (bmax - bmin) < lim * bmin;
+}
+
+// Phase B: every unordered pair of this thread's line.
+template <typename T, int N, class C, bool SERIES>
+__device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
+                                       const LineTask<N, C> &L,
+                                       const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
+                                       T (&acc)[N + 1][5])
 {
     constexpr int Nq = N + 1, NODES = Shape<N, C>::kNodes;
     if constexpr (C::kCacheLine) {
@@ -547,7 +600,7 @@ __device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const L
         for (int a = 0; a < Nq - 1; ++a)
 #pragma unroll
             for (int l = a + 1; l < Nq; ++l)
-                pair_update(V[a], V[l], D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+                pair_update<T, SERIES>(V[a], V[l], D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
         return;
     }
 #pragma unroll
@@ -571,9 +624,24 @@ __device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const L
             } else {
                 Y.n1 = lm[l][0]; Y.n2 = lm[l][1]; Y.n3 = lm[l][2];
             }
-            pair_update(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+            pair_update<T, SERIES>(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
         }
     }
+}
+
+// Phase B.  With SPLIT the form is chosen once per wave: when every line of
+// the wave is within the series threshold (smooth flow), the pairs skip the
+// log branch and the selects; otherwise each pair selects for itself.  Both
+// forms give the same values.
+template <typename T, int N, class C, bool SPLIT>
+__device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const LineTask<N, C> &L,
+                                  const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
+                                  T (&acc)[N + 1][5])
+{
+    if (SPLIT && __all(line_in_series<T, N, C>(lds, L)))
+        line_pairs_form<T, N, C, true>(lds, D, L, lm, acc);
+    else
+        line_pairs_form<T, N, C, false>(lds, D, L, lm, acc);
 }
 
 // Source term h of the whole right-hand side: the Coriolis term of the
@@ -714,7 +782,8 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     if constexpr (SURF) {
         if (active) surface_ends<T, N, C>(lds, L, lm, face, nelem, acc);
     }
-    if (active) line_pairs<T, N, C>(lds, D, L, lm, acc);
+    constexpr bool kSplit = SURF ? C::kSeriesFormSurf : C::kSeriesForm;
+    if (active) line_pairs<T, N, C, kSplit>(lds, D, L, lm, acc);
     __syncthreads();  // node values are dead from here on: LDS becomes the partials
 
     // phases C, D

@@ -1,0 +1,126 @@
+"""The two forms of the pair loop give bitwise equal results.
+
+Where every line of a wave is within the series threshold of the log means
+(page: GPU Performance of an Entropy-Stable DG Euler Solver with
+Non-Conservative Terms, section 4.1, the log mean with its series branch), the
+kernel runs a pair loop without the log branch and the selects; otherwise
+each pair selects for itself.  The volume term is element-local, so a large
+density jump at one node of one element (which sends every wave holding that
+element's lines to the general form) must leave every other element's
+result bitwise unchanged, although the waves shared with the perturbed
+element now evaluate those elements' pairs with the other form (the host
+checks that premise from the state: every xi1 and xi2 line of the base
+state is within the series range, some of the perturbed element's are not).  The whole
+right-hand side couples face neighbours, so there the comparison excludes the
+perturbed element and its six face neighbours.  Both runs are also held to
+the oracle at the parity tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import esdg
+from entropy_stable_dg_amd import inputs as I
+from tests.test_gpu_parity import dev, to_gpu
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float64: 1e-11, np.float32: 2e-5}
+
+
+def smooth_workload(N, dtype):
+    wl = I.build_workload(f"series_N{N}", (6, 5, 4), (0, 0, 0), (1000, 1000, 1000), N, "bubble",
+                          seed=900 + N, warp_frac=0.05, periodic=(True, True, False))
+    q, phi, geom, D = (a.astype(dtype) for a in (wl.q, wl.phi, wl.geom, wl.D))
+    return q, phi, geom, D, wl.nbr
+
+
+def perturb(q, e, node):
+    """Scale the whole state of one node by 1.5: same velocity and b = rho/(2p),
+    a 50 % density jump to its neighbours along every line through it."""
+    p = q.copy()
+    p[:, e, node] *= 1.5
+    return p
+
+
+def lines_in_series(q, phi, N, eps):
+    """Per (element, direction, line): whether rho and b = rho/(2p) vary along
+    the line by less than the kernel's sufficient bound 0.99 * 2 eps min (the
+    premise of the series form), from the host state."""
+    q = q.astype(np.float64)
+    rho = q[0]
+    p = 0.4 * (q[4] - 0.5 * (q[1] ** 2 + q[2] ** 2 + q[3] ** 2) / rho - rho * phi.astype(np.float64))
+    b = rho / (2 * p)
+    Nq = N + 1
+    out = []
+    for v in (rho, b):
+        g = v.reshape(-1, Nq, Nq, Nq)           # [e][c][b][a], node a + Nq (b + Nq c)
+        ok = []
+        for ax in (3, 2, 1):                     # lines along xi1, xi2, xi3
+            lo, hi = g.min(axis=ax), g.max(axis=ax)
+            ok.append((hi - lo) < 0.99 * 2 * eps * lo)
+        out.append(np.stack(ok))
+    return out[0] & out[1]
+
+
+def run(q, phi, geom, D, nbr=None):
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    if nbr is None:
+        out = esdg.volume_rhs(tq, tp, tg, tD)
+    else:
+        out = esdg.rhs(tq, tp, tg, tD, torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev()))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def held_to_oracle(got, q, phi, geom, D, N, tol, nbr=None):
+    if nbr is None:
+        ref = oracle.volume_rhs(q, phi, geom, D, N)
+        scale = np.abs(ref).reshape(5, -1).max(axis=1)
+    else:
+        ref, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+        scale = np.abs(mag).reshape(5, -1).max(axis=1)
+    err = np.abs(got.astype(np.float64) - ref).reshape(5, -1).max(axis=1) / scale
+    assert np.all(np.isfinite(got))
+    assert err.max() <= tol, err
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("N", [3, 4, 5, 7])
+def test_volume_term_forms_agree(N, dtype):
+    q, phi, geom, D, _ = smooth_workload(N, dtype)
+    nelem = q.shape[1]
+    e, node = 37 % nelem, ((N + 1) ** 3) // 2
+    eps = 1e-2 if dtype == np.float64 else 1e-1
+    qp = perturb(q, e, node)
+    # base: every line along xi1 and xi2 in series range (the xi3 lines of
+    # these 250 m tall elements cross a ~3 % density change, beyond the fp64
+    # threshold); perturbed: element e has xi1/xi2 lines that are not, so the
+    # waves holding them switch to the general form
+    assert lines_in_series(q, phi, N, eps)[:2].all()
+    assert not lines_in_series(qp, phi, N, eps)[:2, e].all()
+    base = run(q, phi, geom, D)
+    pert = run(qp, phi, geom, D)
+    others = np.arange(nelem) != e
+    print(f"[series] N={N} {np.dtype(dtype).name}: element {e} perturbed; "
+          f"it changed {not np.array_equal(base[:, e], pert[:, e])}", flush=True)
+    assert not np.array_equal(base[:, e], pert[:, e])
+    assert np.array_equal(base[:, others], pert[:, others])
+    held_to_oracle(base, q, phi, geom, D, N, TOL[dtype])
+    held_to_oracle(pert, qp, phi, geom, D, N, TOL[dtype])
+
+
+@pytest.mark.parametrize("N,dtype", [(4, np.float32), (5, np.float64), (7, np.float64), (7, np.float32)])
+def test_whole_rhs_forms_agree(N, dtype):
+    q, phi, geom, D, nbr = smooth_workload(N, dtype)
+    nelem = q.shape[1]
+    e, node = 37 % nelem, ((N + 1) ** 3) // 2
+    base = run(q, phi, geom, D, nbr)
+    qp = perturb(q, e, node)
+    pert = run(qp, phi, geom, D, nbr)
+    touched = {e} | {int(n) for n in nbr[e] if n >= 0}
+    keep = np.array([i not in touched for i in range(nelem)])
+    assert np.array_equal(base[:, keep], pert[:, keep])
+    held_to_oracle(base, q, phi, geom, D, N, TOL[dtype], nbr)
+    held_to_oracle(pert, qp, phi, geom, D, N, TOL[dtype], nbr)
