@@ -509,7 +509,7 @@ def main() -> int:
         "frac_fp64_vector_peak_counted": (counted_flops / t_cold / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                           if counted_flops else None),
         "hbm_gbs_counted": traffic / t_cold / 1e9 if traffic else None,
-        "binding_roof": "HBM at scale (88 % of the measured stream at 262,144 elements); at this "
+        "binding_roof": "HBM at scale (about 91 % of the measured stream at 262,144 elements); at this "
                         "size the first round of workgroups' loads cannot overlap compute",
         "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
         "hot_ms_per_step": t_hot * 1e3,
