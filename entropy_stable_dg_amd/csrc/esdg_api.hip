@@ -29,15 +29,15 @@ template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };         
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true>; };          // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
-template <> struct Launch<double, 5> { using C = LaunchCfg<1, 128, 0, true, false, false, false, true, true>; };     // 108/128
+template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, true>; };    // 216/256
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, false, false, true>; };          // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true>; };      // 192/192
-template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256>; };                        // 243/256
+template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
 template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, false, false, true, true>; };
 template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true>; };
-template <> struct Launch<float, 5> { using C = LaunchCfg<1, 128, 0, false, false, false, false, true>; };
+template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, false, false, true, true>; };
