@@ -118,6 +118,18 @@ def test_every_order_random_state(N, dtype):
     check(got, ref, TOL[dtype], f"random N={N} {np.dtype(dtype).name}")
 
 
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_every_order_ragged_workgroup(N, dtype):
+    """Five elements: the last workgroup is partly empty for every
+    elements-per-workgroup count of the launch table (16, 7, 4, 3, 2, 1)."""
+    q, phi, geom, D = random_workload(N, nelem_xyz=(5, 1, 1), seed=50 + N)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_rhs(q, phi, geom, D)
+    ref = oracle.volume_rhs(q, phi, geom, D, N)
+    check(got, ref, TOL[dtype], f"ragged 5 elements N={N} {np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("N", [3, 4, 7])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_log_branch_stress(N, dtype):

@@ -98,6 +98,18 @@ def test_every_order(N, dtype):
     check_full(got, ref, mag, TOL[dtype], f"N={N} {np.dtype(dtype).name} periodic={periodic}")
 
 
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_every_order_ragged_workgroup(N, dtype):
+    """Five elements in a row (periodic along it, slip walls elsewhere): the
+    last workgroup is partly empty for every elements-per-workgroup count."""
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, (5, 1, 1), (True, False, False), seed=60 + N)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_full_rhs(q, phi, geom, D, nbr)
+    ref, mag = oracle.rhs(q, phi, geom, D, nbr, N, with_magnitude=True)
+    check_full(got, ref, mag, TOL[dtype], f"ragged 5 elements N={N} {np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("K", [(7, 1, 1), (5, 1, 2), (1, 1, 1)])
 def test_ragged_and_self_neighbour_meshes(K):
     """Element counts that leave the last workgroup partly empty, and a single

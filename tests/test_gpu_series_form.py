@@ -9,8 +9,10 @@ density jump at one node of one element (which sends every wave holding that
 element's lines to the general form) must leave every other element's
 result bitwise unchanged, although the waves shared with the perturbed
 element now evaluate those elements' pairs with the other form (the host
-checks that premise from the state: every xi1 and xi2 line of the base
-state is within the series range, some of the perturbed element's are not).  The whole
+checks that premise from the state: every line of the base state is within
+the series range, and the perturbed element has lines outside it in every
+direction).  The 125-element mesh leaves the last workgroup partly empty for
+the launch shapes of N = 3, 4 and 5.  The whole
 right-hand side couples face neighbours, so there the comparison excludes the
 perturbed element and its six face neighbours.  Both runs are also held to
 the oracle at the parity tolerance.
@@ -30,7 +32,7 @@ TOL = {np.float64: 1e-11, np.float32: 2e-5}
 
 
 def smooth_workload(N, dtype):
-    wl = I.build_workload(f"series_N{N}", (6, 5, 4), (0, 0, 0), (1000, 1000, 1000), N, "bubble",
+    wl = I.build_workload(f"series_N{N}", (5, 5, 5), (0, 0, 0), (1000, 1000, 1000), N, "bubble",
                           seed=900 + N, warp_frac=0.05, periodic=(True, True, False))
     q, phi, geom, D = (a.astype(dtype) for a in (wl.q, wl.phi, wl.geom, wl.D))
     return q, phi, geom, D, wl.nbr
@@ -94,12 +96,12 @@ def test_volume_term_forms_agree(N, dtype):
     e, node = 37 % nelem, ((N + 1) ** 3) // 2
     eps = 1e-2 if dtype == np.float64 else 1e-1
     qp = perturb(q, e, node)
-    # base: every line along xi1 and xi2 in series range (the xi3 lines of
-    # these 250 m tall elements cross a ~3 % density change, beyond the fp64
-    # threshold); perturbed: element e has xi1/xi2 lines that are not, so the
+    # base: every line in series range (the 200 m tall elements cross about
+    # 1.6 % of density change vertically, inside the fp64 bound of 1.98 %);
+    # perturbed: element e has lines in every direction that are not, so the
     # waves holding them switch to the general form
-    assert lines_in_series(q, phi, N, eps)[:2].all()
-    assert not lines_in_series(qp, phi, N, eps)[:2, e].all()
+    assert lines_in_series(q, phi, N, eps).all()
+    assert not lines_in_series(qp, phi, N, eps)[:, e].all(axis=(1, 2)).any()
     base = run(q, phi, geom, D)
     pert = run(qp, phi, geom, D)
     others = np.arange(nelem) != e
