@@ -7,7 +7,7 @@ Two levels:
     include/esdg.h under the same names (device pointers as Python ints, a
     status code returned);
   * volume_rhs(q, phi, geom, D, out=None, stream=None) and
-    rhs(q, phi, geom, D, nbr, out=None, stream=None) -- the same calls on
+    rhs(q, phi, geom, D, nbr, omega=None, out=None, stream=None) -- the same calls on
     torch tensors resident on the GPU, raising EsdgError on a bad status.
 """
 from __future__ import annotations
