@@ -31,7 +31,11 @@
 //     the symmetric contravariant flux S~ serves both nodes, the gravity part
 //     is g/b_a for node a and -g/b_l for node l.  Both contributions are
 //     accumulated in registers, so there is no cross-thread scatter, no load
-//     imbalance and no duplicated antipodal pair at any N.
+//     imbalance and no duplicated antipodal pair at any N.  Where every line
+//     of a wave lies within the log means' series threshold (one wave vote,
+//     a per-order launch option), the wave runs a second copy of the pair
+//     loop without the log branch and its selects; both copies give the same
+//     values.
 //   * Phase C: each line writes its Nq x 5 partial sums to LDS (one array per
 //     direction, every slot written by exactly one thread: no atomics, the
 //     result is bitwise reproducible).
