@@ -447,6 +447,13 @@ def main() -> int:
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                       if inf["dtype"] == "f64" else None),
         }
+        if inf["dtype"] == "f32":
+            fl32 = measured_counter(key.replace(":", "_"), inf["dtype"], "fp32_flops_per_launch")
+            extra[key]["frac_fp32_vector_peak"] = (inf["flops"] / c / 1e12
+                                                   / perfmodel.PEAK_FP32_VECTOR_TFLOPS)
+            extra[key]["gflops_counted_fp32"] = fl32 / c / 1e9 if fl32 else None
+            extra[key]["frac_fp32_vector_peak_counted"] = (
+                fl32 / c / 1e12 / perfmodel.PEAK_FP32_VECTOR_TFLOPS if fl32 else None)
         if mode == "graph":
             extra[key]["what"] = "the same launches captured once in a HIP graph and replayed"
         if full:
