@@ -107,6 +107,7 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
         fn = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
     else:
         fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
+        fn_rhs = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
     ptrs = [(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), nbr.data_ptr(),
@@ -258,12 +259,15 @@ def time_ablation(steps: int, warmup: int) -> dict:
 
 def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"),
                    steps: int = 20) -> dict:
-    """Throughput of the volume term at every order N and refinement level L
-    (N_e = 2^(3L) elements, one base element as in the page's Fig. 3 and
-    Fig. 5): the bubble-shaped state on a warped 8^3 mesh (L = 3) is built on
-    the host once per order and tiled on the GPU to reach L = 4..6 (the kernel
-    is element-local, so tiling leaves the work and traffic per element
-    unchanged).  Below 512 MB of footprint, launches rotate over enough copies
+    """Throughput of the volume term and of the whole right-hand side at every
+    order N and refinement level L (N_e = 2^(3L) elements, one base element as
+    in the page's Fig. 3 and Fig. 5): the bubble-shaped state on a warped 8^3
+    mesh (L = 3; periodic in x and y, slip walls in z) is built on the host
+    once per order and tiled on the GPU to reach L = 4..6.  The volume term is
+    element-local, so tiling leaves its work and traffic per element
+    unchanged; for the whole right-hand side every tile keeps the base mesh's
+    connectivity (offset to its own elements), so each tile is a closed mesh
+    of its own.  Below 512 MB of footprint, launches rotate over enough copies
     that inputs are not cache-resident."""
     import torch
 
@@ -274,11 +278,13 @@ def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"
     points = []
     for dtype in dtypes:
         fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
+        fn_rhs = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
         for N in orders:
             wl = inputs.build_workload(f"sweep_N{N}", (8, 8, 8), (0, 0, 0), (1000, 1000, 1000), N,
                                        "bubble", seed=600 + N, warp_frac=0.05, dtype=dtype,
                                        periodic=(True, True, False))
             base = [torch.from_numpy(a).to(dev) for a in (wl.q, wl.phi, wl.geom, wl.D)]
+            base_nbr = torch.from_numpy(wl.nbr).to(dev)
             for L in levels:
                 reps = 8 ** (L - 3)
                 q = base[0].repeat(1, reps, 1)
@@ -293,20 +299,37 @@ def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"
                     sets.append((q.clone(), phi.clone(), geom.clone(), torch.empty_like(q)))
                 ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), r.data_ptr()) for a, b, c, r in sets]
 
-                def run(k: int) -> None:
+                # each tile is a closed mesh of its own: its face neighbours
+                # are the base mesh's, offset by the tile's first element
+                base_ne = base[0].shape[1]
+                nbr = torch.cat([torch.where(base_nbr >= 0, base_nbr + t * base_ne, base_nbr)
+                                 for t in range(reps)]).contiguous()
+                assert nbr.dtype == torch.int32 and tuple(nbr.shape) == (nelem, 6)
+                assert int(nbr.max()) < nelem
+
+                def run(k: int, full: bool = False) -> None:
                     for i in range(k):
                         p = ptrs[i % nsets]
-                        if fn(p[0], p[1], p[2], D.data_ptr(), N, nelem, p[3], handle) != 0:
-                            raise RuntimeError("volume term launch failed")
+                        if full:
+                            st = fn_rhs(p[0], p[1], p[2], D.data_ptr(), nbr.data_ptr(), None, N, nelem,
+                                        p[3], handle)
+                        else:
+                            st = fn(p[0], p[1], p[2], D.data_ptr(), N, nelem, p[3], handle)
+                        if st != 0:
+                            raise RuntimeError("launch failed")
 
-                run(3)
-                torch.cuda.synchronize()
-                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t0.record()
-                run(steps)
-                t1.record()
-                torch.cuda.synchronize()
-                sec = t0.elapsed_time(t1) * 1e-3 / steps
+                def timed(full: bool) -> float:
+                    run(3, full)
+                    torch.cuda.synchronize()
+                    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    t0.record()
+                    run(steps, full)
+                    t1.record()
+                    torch.cuda.synchronize()
+                    return t0.elapsed_time(t1) * 1e-3 / steps
+
+                sec = timed(False)
+                sec_rhs = timed(True)
                 dof = nelem * (N + 1) ** 3
                 flops = perfmodel.flops_per_element(N) * nelem
                 nbytes = perfmodel.algorithmic_bytes(N, nelem, dtype)
@@ -316,13 +339,18 @@ def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"
                       "arithmetic_intensity": perfmodel.arithmetic_intensity(N, dtype)}
                 if dtype == "f64":
                     pt["frac_fp64_vector_peak"] = pt["analytic_tflops"] / perfmodel.PEAK_FP64_VECTOR_TFLOPS
+                pt["rhs_us"] = sec_rhs * 1e6
+                pt["rhs_gdof_s"] = dof / sec_rhs / 1e9
+                pt["rhs_hbm_gbs"] = perfmodel.algorithmic_bytes_rhs(N, nelem, dtype) / sec_rhs / 1e9
                 points.append(pt)
                 log(f"sweep {dtype} N={N} L={L}: {nelem} el., {pt['us']:.1f} us, {pt['gdof_s']:.2f} GDOF/s, "
-                    f"{pt['analytic_tflops']:.2f} TF/s, {pt['hbm_gbs']:.0f} GB/s")
+                    f"{pt['analytic_tflops']:.2f} TF/s, {pt['hbm_gbs']:.0f} GB/s; whole rhs "
+                    f"{pt['rhs_us']:.1f} us, {pt['rhs_gdof_s']:.2f} GDOF/s")
                 del sets, q, phi, geom
                 torch.cuda.empty_cache()
             del base
-    return {"sweep": "volume term, every order and refinement level (N_e = 2^(3L))",
+    return {"sweep": "volume term and whole right-hand side, every order and refinement level "
+                     "(N_e = 2^(3L))",
             "steps": steps, "points": points}
 
 
