@@ -79,6 +79,16 @@ def measured_counter(workload: str, dtype: str, field: str):
     return rec.get(field)
 
 
+def counted_fp64_flops(workload: str, dtype: str):
+    """Counted FP64 FLOPs per launch (ADD + MUL + TRANS + 2 FMA, x 64 lanes:
+    SQ_INSTS_VALU_FLOPS_FP64 plus SQ_INSTS_VALU_FLOPS_FP64_TRANS) from the
+    committed counter summaries, if taken on the current kernel code."""
+    fl = measured_counter(workload, dtype, "fp64_flops_per_launch")
+    if not fl:
+        return None
+    return fl + (measured_counter(workload, dtype, "fp64_trans_flops_per_launch") or 0.0)
+
+
 def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False,
                   graph: bool = False):
     """Returns (seconds per step rotating cold buffers, seconds per step hot, info).
@@ -374,6 +384,21 @@ def cpu_one_core(wl, seconds: float) -> dict:
             "sample": f"{reps} evaluations of the first {ne} elements of {wl.name}"}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo) and the logical CPUs
+    the OS reports."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs reported)"
+
+
 def cpu_baseline(wl, min_seconds: float):
     import oracle
 
@@ -390,7 +415,8 @@ def cpu_baseline(wl, min_seconds: float):
     log(f"cpu oracle: {reps} full evaluations in {dt:.1f} s on {threads} threads -> {value:.3e} DOF/s")
     return {"value": value, "unit": "DOF-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} evaluations of the whole {wl.name} workload ({wl.dof} DOF each), "
-                      f"{dt:.1f} s, fp64 ordered pairs, OpenMP over elements"}
+                      f"{dt:.1f} s, fp64 ordered pairs, OpenMP over elements",
+            "cpu": cpu_model()}
 
 
 def main() -> int:
@@ -452,7 +478,7 @@ def main() -> int:
     achieved_gbs = info["bytes"] / t_cold / 1e9
     gflops = info["flops"] / t_cold / 1e9
     traffic = measured_traffic(HEADLINE, info["dtype"])
-    counted_flops = measured_counter(HEADLINE, info["dtype"], "fp64_flops_per_launch")
+    counted_flops = counted_fp64_flops(HEADLINE, info["dtype"])
 
     extra = {}
     names = [x for x in args.extra.split(",") if x]
@@ -469,7 +495,7 @@ def main() -> int:
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
             "traffic": measured_traffic(key.replace(":", "_"), inf["dtype"]),
             "gflops_counted_fp64": (lambda fl: fl / c / 1e9 if fl else None)(
-                measured_counter(key.replace(":", "_"), inf["dtype"], "fp64_flops_per_launch")),
+                counted_fp64_flops(key.replace(":", "_"), inf["dtype"])),
             "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
             "hbm_frac": inf["bytes"] / c / 1e9 / perfmodel.PEAK_HBM_GBS,
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
