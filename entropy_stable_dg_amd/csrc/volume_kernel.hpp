@@ -561,7 +561,9 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
 // True when every pair of this thread's line takes the series form of both
 // log means: any pair's jump is at most max - min along the line and its sum
 // at least 2 min, so (max - min) < 2 eps min implies the per-pair test; the
-// 1 % margin covers that test's rounding.  NaN states give false.
+// 1 % margin covers that test's rounding.  Non-positive or infinite states
+// give false; fmin/fmax skip a NaN state, but a NaN node makes every pair of
+// its line NaN in either form, so the forms still agree.
 template <typename T, int N, class C>
 __device__ inline bool line_in_series(const T *lds, const LineTask<N, C> &L)
 {
