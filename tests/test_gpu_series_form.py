@@ -126,3 +126,27 @@ def test_whole_rhs_forms_agree(N, dtype):
     assert np.array_equal(base[:, keep], pert[:, keep])
     held_to_oracle(base, q, phi, geom, D, N, TOL[dtype], nbr)
     held_to_oracle(pert, qp, phi, geom, D, N, TOL[dtype], nbr)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("N", [4, 7])
+def test_nan_state_stays_on_its_lines(N, dtype):
+    """A NaN in one node's state reaches exactly the nodes that share one of
+    its three lines (every pair on those lines involves it); every other
+    value, in that element and elsewhere, is bitwise that of the clean run,
+    whichever form the waves take."""
+    q, phi, geom, D, _ = smooth_workload(N, dtype)
+    nelem, Nq = q.shape[1], N + 1
+    e, (a0, b0, c0) = 37 % nelem, (1, 2, 3 % Nq)
+    node = a0 + Nq * (b0 + Nq * c0)
+    qn = q.copy()
+    qn[0, e, node] = np.nan
+    base = run(q, phi, geom, D)
+    got = run(qn, phi, geom, D)
+    a, b, c = np.meshgrid(np.arange(Nq), np.arange(Nq), np.arange(Nq), indexing="ij")
+    on_line = ((b == b0) & (c == c0)) | ((a == a0) & (c == c0)) | ((a == a0) & (b == b0))
+    poisoned = np.zeros((nelem, Nq ** 3), dtype=bool)
+    poisoned[e, (a + Nq * (b + Nq * c))[on_line]] = True
+    assert np.isnan(got[:, poisoned]).all()
+    assert np.array_equal(got[:, ~poisoned], base[:, ~poisoned])
+
