@@ -198,6 +198,36 @@ def test_non_default_stream(workloads):
     assert torch.equal(got, ref)
 
 
+def test_concurrent_streams_are_independent(workloads):
+    """The library keeps no state: launches of both entry points, in both
+    precisions, in flight at once on four streams give bitwise the results
+    of one-at-a-time calls."""
+    cases = []
+    for name, full in (("bubble", False), ("baroclinic", True), ("tiny", False), ("bubble_f32", True)):
+        wl = get(workloads, name)
+        arrays = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+        nbr = torch.from_numpy(wl.nbr).to(dev()) if full else None
+        cases.append((arrays, nbr))
+
+    def call(arrays, nbr, stream=None):
+        if nbr is None:
+            return esdg.volume_rhs(*arrays, stream=stream)
+        return esdg.rhs(*arrays, nbr, omega=(0.0, 0.0, 1e-4), stream=stream)
+
+    ref = [call(a, n) for a, n in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in cases]
+    main = torch.cuda.current_stream()
+    outs = []
+    for (a, n), s in zip(cases, streams):
+        s.wait_stream(main)
+        with torch.cuda.stream(s):
+            outs.append(call(a, n, stream=s))
+    torch.cuda.synchronize()
+    for got, want in zip(outs, ref):
+        assert torch.equal(got, want)
+
+
 def test_full_size_mesh_by_element_locality(workloads):
     """The pages' N=4, L=6 bubble mesh size (262,144 elements, 32,768,000 DOF):
     the bubble workload tiled 64 times must give the small run's result, tiled,
