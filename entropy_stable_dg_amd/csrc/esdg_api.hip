@@ -21,17 +21,26 @@ constexpr int kMaxOrder = 8;
 // N=4 L=6 mesh sizes; the series form where it measured faster at the
 // 4096- and 32,768-element sizes (it adds registers: at N <= 2 it gains
 // nothing, and the fp64 N = 8 kernel would spill).
+//
+// At N = 3 and N = 7 (N+1 a power of two) the unpadded LDS node grid puts
+// the lanes of a direction-1 or direction-2 line read on a few banks (up to
+// 16 lanes per bank at N = 7); one pad value per row (N = 7) or three per
+// plane (fp64 N = 3) spread them, for 12.5 % and 19 % more LDS.  The other
+// orders gained nothing measurable from padding (N + 1 odd, or the waves
+// already mix directions), and fp32 N = 3 and N = 5 pads were neutral to
+// slower.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, direction-major line order, direction-3 lines finish the nodes,
-// series form (volume term), series form (with the surface term)>
+// series form (volume term), series form (with the surface term), LDS pad
+// per row, per plane (per element)>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
-template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true>; };          // 192/192
+template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, true>; };    // 216/256
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, false, false, true>; };          // 147/192
-template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true>; };      // 192/192
+template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
@@ -39,7 +48,7 @@ template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false
 template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
-template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
+template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true, 1>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, false, false, true, true>; };
 
 template <typename T, int N, bool SURF>

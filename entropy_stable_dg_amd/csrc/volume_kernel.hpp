@@ -146,7 +146,9 @@ __device__ inline float select(bool c, float a, float b)
     return __builtin_bit_cast(float, c ? ua : ub);
 }
 
-// Values staged per node in LDS (field-major: value v of node t at v*NODES+t).
+// Values staged per node in LDS, field-major: value v of node t at
+// v*SLOTS + slot(t), where slot() may pad rows, planes and elements of the
+// node grid (Shape below).
 // Scaled where the pair only needs a pair mean or a jump, so the pair does
 // not multiply by constants: kU1..kU3 hold u/2 (X.u + Y.u = {{u}}), kW holds
 // w/2 with w = phi - |u|^2/2 (the energy flux needs {{w}} only), kPhi holds
@@ -163,7 +165,8 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 // SIMD (it then caps the registers); METRIC_LDS stages the metric terms in
 // LDS (coalesced loads in phase A) instead of loading them per line thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
-          bool KMAJOR_ = false, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false>
+          bool KMAJOR_ = false, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
+          int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -184,6 +187,13 @@ struct LaunchCfg {
     // registers); SERIES_SURF the same for the kernel with the surface term.
     static constexpr bool kSeriesForm = SERIES_;
     static constexpr bool kSeriesFormSurf = SERIES_SURF_;
+    // Padding of the LDS node grid (in values): after every row of N+1
+    // nodes along xi_1, every plane and every element.  Lines read LDS at a
+    // fixed slot stride per direction, and the pads change those strides so
+    // that the 64 lanes of a wave spread over the LDS banks.
+    static constexpr int kRowPad = ROW_PAD_;
+    static constexpr int kPlanePad = PLANE_PAD_;
+    static constexpr int kElemPad = ELEM_PAD_;
 };
 
 template <int N, class C>
@@ -192,6 +202,12 @@ struct Shape {
     static constexpr int Nq2 = Nq * Nq;
     static constexpr int Np = Nq2 * Nq;
     static constexpr int kNodes = C::EPB * Np;          // nodes per workgroup
+    // LDS slot strides of the node grid: x + kRow y + kPlane z + kElem eb
+    static constexpr int kRow = Nq + C::kRowPad;
+    static constexpr int kPlane = Nq * kRow + C::kPlanePad;
+    static constexpr int kElem = Nq * kPlane + C::kElemPad;
+    static constexpr bool kPadded = kElem != Np;
+    static constexpr int kSlots = C::EPB * kElem;       // LDS slots per staged value
     static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
     static constexpr int kNodeIters = (kNodes + C::NT - 1) / C::NT;  // nodes per thread
     static constexpr int kStaged = C::kMetricInLds ? kNodeValues : kJa;
@@ -199,30 +215,42 @@ struct Shape {
     static constexpr int kRegion = kStaged > kPartials ? kStaged : kPartials;
     // with FIN, -1/J of every node is staged after the shared region
     static constexpr int kMinusInvJ = kRegion;
-    static constexpr int kLdsValues = (kRegion + (C::kFinalizeInLine ? 1 : 0)) * kNodes;
+    static constexpr int kLdsValues = (kRegion + (C::kFinalizeInLine ? 1 : 0)) * kSlots;
     static_assert(kLines <= C::NT, "one line task per thread");
+    static_assert(C::kRowPad >= 0 && C::kPlanePad >= 0 && C::kElemPad >= 0, "pads");
+    // LDS slot of node t of the workgroup (t = eb Np + x + Nq y + Nq^2 z)
+    __device__ static inline int slot(int t) {
+        if constexpr (!kPadded) {
+            return t;
+        } else {
+            const int eb = t / Np, r = t - eb * Np;
+            const int z = r / Nq2, r2 = r - z * Nq2;
+            const int y = r2 / Nq, x = r2 - y * Nq;
+            return eb * kElem + z * kPlane + y * kRow + x;
+        }
+    }
 };
 
 // One node's staged values, read from LDS where a pair needs them.
 template <typename T>
 struct NodeRegs {
     T rho, u1, u2, u3, b, lrho, lb, ph, w, ib, n1, n2, n3;
-    __device__ inline void load_state(const T *lds, int NODES, int s) {
-        rho = lds[kRho * NODES + s];
-        u1 = lds[kU1 * NODES + s];
-        u2 = lds[kU2 * NODES + s];
-        u3 = lds[kU3 * NODES + s];
-        b = lds[kB * NODES + s];
-        lrho = lds[kLogRho * NODES + s];
-        lb = lds[kLogB * NODES + s];
-        ph = lds[kPhi * NODES + s];
-        w = lds[kW * NODES + s];
-        ib = lds[kInvB * NODES + s];
+    __device__ inline void load_state(const T *lds, int SLOTS, int s) {
+        rho = lds[kRho * SLOTS + s];
+        u1 = lds[kU1 * SLOTS + s];
+        u2 = lds[kU2 * SLOTS + s];
+        u3 = lds[kU3 * SLOTS + s];
+        b = lds[kB * SLOTS + s];
+        lrho = lds[kLogRho * SLOTS + s];
+        lb = lds[kLogB * SLOTS + s];
+        ph = lds[kPhi * SLOTS + s];
+        w = lds[kW * SLOTS + s];
+        ib = lds[kInvB * SLOTS + s];
     }
-    __device__ inline void load_metric(const T *lds, int NODES, int s, int k) {
-        n1 = lds[(kJa + 3 * k + 0) * NODES + s];
-        n2 = lds[(kJa + 3 * k + 1) * NODES + s];
-        n3 = lds[(kJa + 3 * k + 2) * NODES + s];
+    __device__ inline void load_metric(const T *lds, int SLOTS, int s, int k) {
+        n1 = lds[(kJa + 3 * k + 0) * SLOTS + s];
+        n2 = lds[(kJa + 3 * k + 1) * SLOTS + s];
+        n3 = lds[(kJa + 3 * k + 2) * SLOTS + s];
     }
 };
 
@@ -359,7 +387,9 @@ struct Batch {
 template <int N, class C>
 struct LineTask {
     using S = Shape<N, C>;
-    int eb, k, nb, step;
+    // nb, step: LDS slot of the line's first node and the slot stride along
+    // the line; n0, nstep: the same in the node numbering of one element
+    int eb, k, nb, step, n0, nstep;
     __device__ inline LineTask() {
         constexpr int Nq = S::Nq, Nq2 = S::Nq2, Np = S::Np;
         const int task = threadIdx.x;
@@ -377,9 +407,35 @@ struct LineTask {
             line = r3 - k * Nq2;
         }
         const int p1 = line % Nq, p2 = line / Nq;
-        const int base = (k == 0) ? Nq * (p1 + Nq * p2) : (k == 1) ? p1 + Nq2 * p2 : p1 + Nq * p2;
-        step = (k == 0) ? 1 : (k == 1) ? Nq : Nq2;
-        nb = eb * Np + base;  // LDS index of the line's first node
+        n0 = (k == 0) ? Nq * (p1 + Nq * p2) : (k == 1) ? p1 + Nq2 * p2 : p1 + Nq * p2;
+        nstep = (k == 0) ? 1 : (k == 1) ? Nq : Nq2;
+        if constexpr (S::kPadded) {
+            constexpr int R = S::kRow, P = S::kPlane;
+            const int base = (k == 0) ? R * p1 + P * p2 : (k == 1) ? p1 + P * p2 : p1 + R * p2;
+            step = (k == 0) ? 1 : (k == 1) ? R : P;
+            nb = eb * S::kElem + base;
+        } else {
+            step = nstep;
+            nb = eb * Np + n0;
+        }
+    }
+    // node index within the workgroup of the line's node a; the line's
+    // first node within its element and the node stride along the line
+    __device__ inline int node(int a) const {
+        if constexpr (S::kPadded) return eb * S::Np + n0 + a * nstep;
+        else return nb + a * step;
+    }
+    __device__ inline int node_base() const {
+        if constexpr (S::kPadded) return eb * S::Np + n0;
+        else return nb;
+    }
+    __device__ inline int first_in_element() const {
+        if constexpr (S::kPadded) return n0;
+        else return nb - eb * S::Np;
+    }
+    __device__ inline int node_step() const {
+        if constexpr (S::kPadded) return nstep;
+        else return step;
     }
     __device__ inline bool active(int nvalid) const {
         return (int)threadIdx.x < S::kLines && eb * S::Np < nvalid;
@@ -450,29 +506,30 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
                                    T (&mJ)[Shape<N, C>::kNodeIters])
 {
     using A = Arith<T>;
-    constexpr int NODES = Shape<N, C>::kNodes;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
 #pragma unroll
     for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
+            const int st = Shape<N, C>::slot(t);
             const NodeRegs<T> V = node_values(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
                                               L.v[it][4], L.v[it][5]);
-            lds[kRho * NODES + t] = V.rho;
-            lds[kU1 * NODES + t] = V.u1;
-            lds[kU2 * NODES + t] = V.u2;
-            lds[kU3 * NODES + t] = V.u3;
-            lds[kB * NODES + t] = V.b;
-            lds[kLogRho * NODES + t] = V.lrho;
-            lds[kLogB * NODES + t] = V.lb;
-            lds[kPhi * NODES + t] = V.ph;
-            lds[kW * NODES + t] = V.w;
-            lds[kInvB * NODES + t] = V.ib;
+            lds[kRho * SLOTS + st] = V.rho;
+            lds[kU1 * SLOTS + st] = V.u1;
+            lds[kU2 * SLOTS + st] = V.u2;
+            lds[kU3 * SLOTS + st] = V.u3;
+            lds[kB * SLOTS + st] = V.b;
+            lds[kLogRho * SLOTS + st] = V.lrho;
+            lds[kLogB * SLOTS + st] = V.lb;
+            lds[kPhi * SLOTS + st] = V.ph;
+            lds[kW * SLOTS + st] = V.w;
+            lds[kInvB * SLOTS + st] = V.ib;
             if constexpr (C::kMetricInLds) {
 #pragma unroll
-                for (int j = 0; j < 9; ++j) lds[(kJa + j) * NODES + t] = L.m[it][j];
+                for (int j = 0; j < 9; ++j) lds[(kJa + j) * SLOTS + st] = L.m[it][j];
             }
             mJ[it] = -A::rcp(L.J[it]);
-            if constexpr (C::kFinalizeInLine) lds[Shape<N, C>::kMinusInvJ * NODES + t] = mJ[it];
+            if constexpr (C::kFinalizeInLine) lds[Shape<N, C>::kMinusInvJ * SLOTS + st] = mJ[it];
         }
     }
 }
@@ -521,7 +578,7 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
                                     const FaceLoads<T> &F, int64_t nelem, T (&acc)[N + 1][5])
 {
     using A = Arith<T>;
-    constexpr int NODES = Shape<N, C>::kNodes;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
     // The surface term at an end node is -(+-1) Ja^k . F*(own, partner) / (w_end J)
     // with the LGL end weight w_end = 2/(N(N+1)); pair_update contracts with
     // Ja^k(own) + Ja^k(partner) = 2 Ja^k(own), so the coefficient is
@@ -531,9 +588,9 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
     for (int end = 0; end < 2; ++end) {
         const int a = end ? N : 0;
         NodeRegs<T> X;
-        X.load_state(lds, NODES, L.nb + a * L.step);
+        X.load_state(lds, SLOTS, L.nb + a * L.step);
         if constexpr (C::kMetricInLds) {
-            X.load_metric(lds, NODES, L.nb + a * L.step, L.k);
+            X.load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
         } else {
             X.n1 = lm[a][0]; X.n2 = lm[a][1]; X.n3 = lm[a][2];
         }
@@ -567,13 +624,13 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
 template <typename T, int N, class C>
 __device__ inline bool line_in_series(const T *lds, const LineTask<N, C> &L)
 {
-    constexpr int NODES = Shape<N, C>::kNodes;
-    T rmin = lds[kRho * NODES + L.nb], rmax = rmin;
-    T bmin = lds[kB * NODES + L.nb], bmax = bmin;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
+    T rmin = lds[kRho * SLOTS + L.nb], rmax = rmin;
+    T bmin = lds[kB * SLOTS + L.nb], bmax = bmin;
 #pragma unroll
     for (int a = 1; a < N + 1; ++a) {
-        const T r = lds[kRho * NODES + L.nb + a * L.step];
-        const T b = lds[kB * NODES + L.nb + a * L.step];
+        const T r = lds[kRho * SLOTS + L.nb + a * L.step];
+        const T b = lds[kB * SLOTS + L.nb + a * L.step];
         rmin = fmin(rmin, r);
         rmax = fmax(rmax, r);
         bmin = fmin(bmin, b);
@@ -590,14 +647,14 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
                                        const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
                                        T (&acc)[N + 1][5])
 {
-    constexpr int Nq = N + 1, NODES = Shape<N, C>::kNodes;
+    constexpr int Nq = N + 1, SLOTS = Shape<N, C>::kSlots;
     if constexpr (C::kCacheLine) {
         NodeRegs<T> V[Nq];
 #pragma unroll
         for (int a = 0; a < Nq; ++a) {
-            V[a].load_state(lds, NODES, L.nb + a * L.step);
+            V[a].load_state(lds, SLOTS, L.nb + a * L.step);
             if constexpr (C::kMetricInLds) {
-                V[a].load_metric(lds, NODES, L.nb + a * L.step, L.k);
+                V[a].load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
             } else {
                 V[a].n1 = lm[a][0]; V[a].n2 = lm[a][1]; V[a].n3 = lm[a][2];
             }
@@ -615,18 +672,18 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
         // keeping the whole line live in registers.
         asm volatile("" ::: "memory");
         NodeRegs<T> X;
-        X.load_state(lds, NODES, L.nb + a * L.step);
+        X.load_state(lds, SLOTS, L.nb + a * L.step);
         if constexpr (C::kMetricInLds) {
-            X.load_metric(lds, NODES, L.nb + a * L.step, L.k);
+            X.load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
         } else {
             X.n1 = lm[a][0]; X.n2 = lm[a][1]; X.n3 = lm[a][2];
         }
 #pragma unroll
         for (int l = a + 1; l < Nq; ++l) {
             NodeRegs<T> Y;
-            Y.load_state(lds, NODES, L.nb + l * L.step);
+            Y.load_state(lds, SLOTS, L.nb + l * L.step);
             if constexpr (C::kMetricInLds) {
-                Y.load_metric(lds, NODES, L.nb + l * L.step, L.k);
+                Y.load_metric(lds, SLOTS, L.nb + l * L.step, L.k);
             } else {
                 Y.n1 = lm[l][0]; Y.n2 = lm[l][1]; Y.n3 = lm[l][2];
             }
@@ -672,13 +729,13 @@ template <typename T, int N, class C>
 __device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool active,
                                       const T (&acc)[N + 1][5])
 {
-    constexpr int NODES = Shape<N, C>::kNodes;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
     if (active && (!C::kFinalizeInLine || L.k < 2)) {
 #pragma unroll
         for (int a = 0; a < N + 1; ++a) {
             const int s = L.nb + a * L.step;
 #pragma unroll
-            for (int f = 0; f < 5; ++f) lds[(L.k * 5 + f) * NODES + s] = acc[a][f];
+            for (int f = 0; f < 5; ++f) lds[(L.k * 5 + f) * SLOTS + s] = acc[a][f];
         }
     }
 }
@@ -691,17 +748,17 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
                                    const T (&acc)[N + 1][5], const T *__restrict__ q,
                                    const Rotation<T> &rot, T *__restrict__ rhs)
 {
-    constexpr int NODES = Shape<N, C>::kNodes;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
     if (active && L.k == 2) {
 #pragma unroll
         for (int a = 0; a < N + 1; ++a) {
             const int s = L.nb + a * L.step;
-            const T mJ = lds[Shape<N, C>::kMinusInvJ * NODES + s];
-            const int64_t g = B.g0 + s;
+            const T mJ = lds[Shape<N, C>::kMinusInvJ * SLOTS + s];
+            const int64_t g = B.g0 + L.node(a);
             T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f)
-                r[f] = (lds[f * NODES + s] + lds[(5 + f) * NODES + s] + acc[a][f]) * mJ;
+                r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + acc[a][f]) * mJ;
             if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
 #pragma unroll
             for (int f = 0; f < 5; ++f) rhs[f * fstride + g] = r[f];
@@ -714,16 +771,17 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
                                  const T (&mJ)[Shape<N, C>::kNodeIters], const T *__restrict__ q,
                                  const Rotation<T> &rot, T *__restrict__ rhs)
 {
-    constexpr int NODES = Shape<N, C>::kNodes;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
 #pragma unroll
     for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
             const int64_t g = B.g0 + t;
+            const int st = Shape<N, C>::slot(t);
             T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f) {
-                const T s = lds[f * NODES + t] + lds[(5 + f) * NODES + t] + lds[(10 + f) * NODES + t];
+                const T s = lds[f * SLOTS + st] + lds[(5 + f) * SLOTS + st] + lds[(10 + f) * SLOTS + st];
                 r[f] = s * mJ[it];
             }
             if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
@@ -768,11 +826,12 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
             for (int a = 0; a < Nq; ++a)
 #pragma unroll
                 for (int j = 0; j < 3; ++j)
-                    lm[a][j] = geom[(3 * L.k + j) * fstride + B.g0 + L.nb + a * L.step];
+                    lm[a][j] = geom[(3 * L.k + j) * fstride + B.g0 + L.node_base() + a * L.node_step()];
         }
     }
     if constexpr (SURF) {
-        if (active) face.template issue_states<N>(q, phi, fstride, nelem, L.nb - L.eb * S::Np, L.step);
+        if (active) face.template issue_states<N>(q, phi, fstride, nelem, L.first_in_element(),
+                                                     L.node_step());
     }
     T mJ[S::kNodeIters];
     stage_nodes<T, N, C>(ld, B, lds, mJ);
