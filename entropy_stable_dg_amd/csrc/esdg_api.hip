@@ -25,26 +25,28 @@ constexpr int kMaxOrder = 8;
 // At N = 3 and N = 7 (N+1 a power of two) the unpadded LDS node grid puts
 // the lanes of a direction-1 or direction-2 line read on a few banks (up to
 // 16 lanes per bank at N = 7); one pad value per row (N = 7) or three per
-// plane (fp64 N = 3) spread them, for 12.5 % and 19 % more LDS.  The other
-// orders gained nothing measurable from padding (N + 1 odd, or the waves
-// already mix directions), and fp32 N = 3 and N = 5 pads were neutral to
-// slower.
+// plane (N = 3; fp32 with four per element and direction-major lines) spread
+// them.  Waves whose lanes hold lines of two directions conflict too: at
+// fp64 N = 6 the 49 lines of each direction start on a 64-lane boundary
+// (order 2), at the same 192 threads.  Other pads and orders were neutral
+// to slower.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
-// registers, direction-major line order, direction-3 lines finish the nodes,
-// series form (volume term), series form (with the surface term), LDS pad
-// per row, per plane (per element)>
+// registers, line order (0 element-major, 1 direction-major, 2 direction-major
+// with each direction on a 32-lane boundary), direction-3 lines finish the
+// nodes, series form (volume term), series form (with the surface term), LDS
+// pad per row, per plane (per element)>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, true>; };    // 216/256
-template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, false, false, true>; };          // 147/192
+template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, 2, false, true>; };          // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
-template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, false, false, true, true>; };
+template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, 1, false, true, true, 0, 3, 4>; };
 template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };

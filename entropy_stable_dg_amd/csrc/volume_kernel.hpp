@@ -165,7 +165,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 // SIMD (it then caps the registers); METRIC_LDS stages the metric terms in
 // LDS (coalesced loads in phase A) instead of loading them per line thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
-          bool KMAJOR_ = false, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
+          int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
           int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
@@ -176,8 +176,11 @@ struct LaunchCfg {
     // LDS reads, more registers); otherwise stream them per pair.
     static constexpr bool kCacheLine = CACHE_;
     // KMAJOR: order line tasks direction-major (all direction-1 lines of the
-    // workgroup first), so each wave reads LDS with one stride pattern.
-    static constexpr bool kDirMajor = KMAJOR_;
+    // workgroup first), so each wave reads LDS with one stride pattern;
+    // KMAJOR = 2 starts each direction on a 32-lane boundary (idle lanes in
+    // between), so that no half-wave mixes lines of two directions.
+    static constexpr bool kDirMajor = KMAJOR_ != 0;
+    static constexpr bool kDirAligned = KMAJOR_ == 2;
     // FIN: the direction-3 line threads finish their own nodes (adding the
     // two other directions' partials from LDS, scaling by -1/J, storing), so
     // LDS holds two directional partials instead of three.
@@ -209,6 +212,9 @@ struct Shape {
     static constexpr bool kPadded = kElem != Np;
     static constexpr int kSlots = C::EPB * kElem;       // LDS slots per staged value
     static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
+    // thread-index stride between the directions' first line tasks
+    static constexpr int kDirStride = C::kDirAligned ? (C::EPB * Nq2 + 31) / 32 * 32 : C::EPB * Nq2;
+    static constexpr int kTaskThreads = C::kDirMajor ? 3 * kDirStride : kLines;
     static constexpr int kNodeIters = (kNodes + C::NT - 1) / C::NT;  // nodes per thread
     static constexpr int kStaged = C::kMetricInLds ? kNodeValues : kJa;
     static constexpr int kPartials = C::kFinalizeInLine ? 10 : kPartialValues;
@@ -216,7 +222,8 @@ struct Shape {
     // with FIN, -1/J of every node is staged after the shared region
     static constexpr int kMinusInvJ = kRegion;
     static constexpr int kLdsValues = (kRegion + (C::kFinalizeInLine ? 1 : 0)) * kSlots;
-    static_assert(kLines <= C::NT, "one line task per thread");
+    static_assert(kTaskThreads <= C::NT, "one line task per thread");
+    static_assert(!C::kDirAligned || C::kDirMajor, "aligned order is direction-major");
     static_assert(C::kRowPad >= 0 && C::kPlanePad >= 0 && C::kElemPad >= 0, "pads");
     // LDS slot of node t of the workgroup (t = eb Np + x + Nq y + Nq^2 z)
     __device__ static inline int slot(int t) {
@@ -395,9 +402,9 @@ struct LineTask {
         const int task = threadIdx.x;
         int line;
         if constexpr (C::kDirMajor) {
-            k = task / (C::EPB * Nq2);
-            const int r = task - k * (C::EPB * Nq2);
-            eb = r / Nq2;
+            k = task / S::kDirStride;
+            const int r = task - k * S::kDirStride;
+            eb = r / Nq2;  // r beyond the direction's lines (aligned order) gives eb >= EPB
             line = r - eb * Nq2;
             if (k > 2) { k = 2; eb = C::EPB; }  // idle thread: marked inactive below
         } else {
@@ -438,7 +445,7 @@ struct LineTask {
         else return step;
     }
     __device__ inline bool active(int nvalid) const {
-        return (int)threadIdx.x < S::kLines && eb * S::Np < nvalid;
+        return (int)threadIdx.x < S::kTaskThreads && eb * S::Np < nvalid;
     }
 };
 
