@@ -426,8 +426,10 @@ struct LineTask {
             nb = eb * Np + n0;
         }
     }
-    // node index within the workgroup of the line's node a; the line's
-    // first node within its element and the node stride along the line
+    // Node numbering for global memory: the workgroup-relative index of the
+    // line's node a (node(a) = node_base() + a node_step()), and the line's
+    // first node within its element.  Without pads the node and slot
+    // numberings coincide.
     __device__ inline int node(int a) const {
         if constexpr (S::kPadded) return eb * S::Np + n0 + a * nstep;
         else return nb + a * step;
