@@ -433,7 +433,7 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE,
                     help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, "
                          "high_order; a ':rhs' suffix profiles the whole right-hand side)")
-    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs",
+    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,high_order",
                     help="comma-separated extra workloads to time (reported under 'extra'); "
                          "a ':rhs' suffix times the whole right-hand side (volume + surface), "
                          "':graph' replays the launches from a captured HIP graph")
