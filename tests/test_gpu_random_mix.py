@@ -51,7 +51,7 @@ def case_inputs(seed):
     return N, dtype, q, phi, geom, D, nbr, int(rough.sum())
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_mixed_waves(seed):
     N, dtype, q, phi, geom, D, nbr, nrough = case_inputs(seed)
     t = [torch.from_numpy(np.ascontiguousarray(a)).to(dev()) for a in (q, phi, geom, D)]
