@@ -36,6 +36,11 @@
 //     a per-order launch option), the wave runs a second copy of the pair
 //     loop without the log branch and its selects; both copies give the same
 //     values.
+//   * LDS layout: field-major, one array per staged value over the node
+//     grid of the workgroup's elements; per-order launch options pad that
+//     grid (per row, plane or element) and start each direction's line
+//     tasks on a 32-lane boundary, so that the lanes of a wave, each reading
+//     one node of its own line, fall on different LDS banks.
 //   * Phase C: each line writes its Nq x 5 partial sums to LDS (one array per
 //     direction, every slot written by exactly one thread: no atomics, the
 //     result is bitwise reproducible).
