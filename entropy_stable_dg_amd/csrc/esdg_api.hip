@@ -29,7 +29,8 @@ constexpr int kMaxOrder = 8;
 // them.  Waves whose lanes hold lines of two directions conflict too: at
 // fp64 N = 6 the 49 lines of each direction start on a 64-lane boundary
 // (order 2), at the same 192 threads.  Other pads and orders were neutral
-// to slower.
+// to slower.  At fp64 N = 5 a 3-wave register cap (168 registers, a
+// 36-byte spill) lets three workgroups share a CU instead of two.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
@@ -40,7 +41,7 @@ template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };         
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
-template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, true>; };    // 216/256
+template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 3, false, false, true, false, true, true>; };    // 216/256
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, 2, false, true>; };          // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
