@@ -29,14 +29,16 @@ constexpr int kMaxOrder = 8;
 // them.  Waves whose lanes hold lines of two directions conflict too: at
 // fp64 N = 6 the 49 lines of each direction start on a 64-lane boundary
 // (order 2), at the same 192 threads.  Other pads and orders were neutral
-// to slower.  At fp64 N = 5 a 3-wave register cap (168 registers, a
-// 36-byte spill) lets three workgroups share a CU instead of two.
+// to slower.  At fp64 N = 5 a 3-wave register cap on the volume kernel (168
+// registers, a 36-byte spill) lets three workgroups share a CU instead of
+// two; at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
+// (96 and 89 registers) does the same for five workgroups instead of four.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
 // with each direction on a 32-lane boundary), direction-3 lines finish the
 // nodes, series form (volume term), series form (with the surface term), LDS
-// pad per row, per plane (per element)>
+// pad per row, per plane, per element, waves hint with the surface term>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
@@ -48,8 +50,8 @@ template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, fal
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
 template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, 1, false, true, true, 0, 3, 4>; };
-template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true>; };
-template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true>; };
+template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 5>; };
+template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true, 1>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, false, false, true, true>; };

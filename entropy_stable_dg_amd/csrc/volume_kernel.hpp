@@ -167,13 +167,13 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 
 // Launch configuration of one kernel instance: EPB elements per workgroup of
 // NT threads; WAVES > 0 asks the compiler to fit at least WAVES waves per
-// SIMD in the volume-term kernel (it then caps the registers; the kernel
-// with the surface term keeps its own count); METRIC_LDS stages the metric
+// SIMD in the volume-term kernel (it then caps the registers), WAVES_SURF the
+// same for the kernel with the surface term; METRIC_LDS stages the metric
 // terms in LDS (coalesced loads in phase A) instead of loading them per line
 // thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
           int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
-          int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0>
+          int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -204,6 +204,7 @@ struct LaunchCfg {
     static constexpr int kRowPad = ROW_PAD_;
     static constexpr int kPlanePad = PLANE_PAD_;
     static constexpr int kElemPad = ELEM_PAD_;
+    static constexpr int WAVES_SURF = WAVES_SURF_;
 };
 
 template <int N, class C>
@@ -812,7 +813,8 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
 // rot.on adds the Coriolis source.
 template <typename T, int N, class C, bool SURF = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
-__attribute__((amdgpu_waves_per_eu(!SURF && C::WAVES > 0 ? C::WAVES : 1)))
+__attribute__((amdgpu_waves_per_eu(SURF ? (C::WAVES_SURF > 0 ? C::WAVES_SURF : 1)
+                                         : (C::WAVES > 0 ? C::WAVES : 1))))
 volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
                   const T *__restrict__ D, const int32_t *__restrict__ nbr, Rotation<T> rot,
                   int64_t nelem, T *__restrict__ rhs)

@@ -70,7 +70,7 @@ def test_bank_model_sees_the_power_of_two_conflict():
     # N = 7, one element, direction-major: unpadded, direction-1 lines start
     # 64 bytes apart, so a 64-bank wave pays several times the
     # conflict-free cycles; one pad value per row brings it near one
-    cfg = dict(zip(L.FIELDS, (1, 192, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0)))
+    cfg = dict(zip(L.FIELDS, (1, 192, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0)))
     plain = L.bank_cost(L.Shape(7, cfg), 2, 64)
     padded = L.bank_cost(L.Shape(7, dict(cfg, row_pad=1)), 2, 64)
     assert plain[0] >= 4 * plain[1]
