@@ -27,8 +27,8 @@ constexpr int kMaxOrder = 8;
 // 16 lanes per bank at N = 7); one pad value per row (N = 7) or three per
 // plane (N = 3; fp32 with four per element and direction-major lines) spread
 // them.  Waves whose lanes hold lines of two directions conflict too: at
-// fp64 N = 6 the 49 lines of each direction start on a 64-lane boundary
-// (order 2), at the same 192 threads.  Other pads and orders were neutral
+// fp64 N = 6 and at N = 2 the 49 or 63 lines of each direction start on a
+// 64-lane boundary (order 2), at the same 192 threads.  Other pads and orders were neutral
 // to slower.  At fp64 N = 5 a 3-wave register cap on the volume kernel (168
 // registers, a 36-byte spill) lets three workgroups share a CU instead of
 // two; at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
@@ -40,7 +40,7 @@ template <typename T, int N> struct Launch;
 // nodes, series form (volume term), series form (with the surface term), LDS
 // pad per row, per plane, per element, waves hint with the surface term>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
-template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192>; };                        // 189/192
+template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };     // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
 template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 3, false, false, true, false, true, true>; };    // 216/256
@@ -48,7 +48,7 @@ template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, fals
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
-template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192>; };
+template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };
 template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, 1, false, true, true, 0, 3, 4>; };
 template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 5>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5>; };
