@@ -32,7 +32,9 @@ constexpr int kMaxOrder = 8;
 // to slower.  At fp64 N = 5 a 3-wave register cap on the volume kernel (168
 // registers, a 36-byte spill) lets three workgroups share a CU instead of
 // two; at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
-// (96 and 89 registers) does the same for five workgroups instead of four.
+// (96 and 89 registers) does the same for five workgroups instead of four,
+// and at fp32 N = 8 direction-3 lines that finish their nodes (32 KB of LDS)
+// with a 4-wave cap on the surface kernel (128 registers) give four.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
@@ -54,7 +56,7 @@ template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, fals
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true, 1>; };
-template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, false, false, true, true>; };
+template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true, true, true, 0, 0, 0, 4>; };
 
 template <typename T, int N, bool SURF>
 int launch(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,
