@@ -33,8 +33,9 @@ constexpr int kMaxOrder = 8;
 // registers, a 36-byte spill) lets three workgroups share a CU instead of
 // two; at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
 // (96 and 89 registers) does the same for five workgroups instead of four,
-// and at fp32 N = 8 direction-3 lines that finish their nodes (32 KB of LDS)
-// with a 4-wave cap on the surface kernel (128 registers) give four.
+// and at fp32 N = 7 and 8 direction-3 lines that finish their nodes (25 and
+// 32 KB of LDS) with 4-wave caps (128 registers) give five and four
+// workgroups per CU instead of four and three.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
@@ -55,7 +56,7 @@ template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false
 template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 5>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
-template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true, 1>; };
+template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 4, false, false, 1, true, true, true, 1, 0, 0, 4>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true, true, true, 0, 0, 0, 4>; };
 
 template <typename T, int N, bool SURF>
