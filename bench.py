@@ -365,15 +365,16 @@ def roofline_sweep(levels=(3, 4, 5, 6), orders=range(1, 9), dtypes=("f64", "f32"
 
 
 def cpu_one_core(wl, seconds: float) -> dict:
-    """The oracle on one host thread over a bounded leading slice of the
-    workload's elements (element-local work, so DOF/s carries over)."""
+    """The oracle's fp64 build on one host thread over a bounded leading slice
+    of the workload's elements (element-local work, so DOF/s carries over)."""
     import oracle
 
+    orc = oracle.fp64()
     ne = max(1, min(wl.nelem, 256))
     q, phi, geom = wl.q[:, :ne], wl.phi[:ne], wl.geom[:, :ne]
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.volume_rhs(q, phi, geom, wl.D, wl.N, threads=1)
+        orc.volume_rhs(q, phi, geom, wl.D, wl.N, threads=1)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
@@ -399,24 +400,36 @@ def cpu_model() -> str:
     return f"{name} ({os.cpu_count()} logical CPUs reported)"
 
 
-def cpu_baseline(wl, min_seconds: float):
+def cpu_baseline(wl, min_seconds: float, runs: int = 3):
+    """The oracle's fp64 build (ordered pairs, OpenMP over elements, every
+    host thread) on the whole workload: `runs` timed runs of at least
+    `min_seconds` / `runs` each, the median reported."""
+    import statistics
+
     import oracle
 
-    threads = oracle.max_threads()
-    oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)  # warm (library load, pages)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N, threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    value = wl.dof * reps / dt
-    log(f"cpu oracle: {reps} full evaluations in {dt:.1f} s on {threads} threads -> {value:.3e} DOF/s")
+    orc = oracle.fp64()
+    threads = orc.max_threads()
+    orc.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N)  # warm (library load, pages)
+    rates, total = [], 0.0
+    for _ in range(runs):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            orc.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N, threads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds / runs:
+                break
+        rates.append(wl.dof * reps / dt)
+        total += dt
+    value = statistics.median(rates)
+    log(f"cpu oracle: {runs} runs, {total:.1f} s on {threads} threads -> median {value:.3e} DOF/s "
+        f"(runs {', '.join(f'{r:.3e}' for r in rates)})")
     return {"value": value, "unit": "DOF-updates/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} evaluations of the whole {wl.name} workload ({wl.dof} DOF each), "
-                      f"{dt:.1f} s, fp64 ordered pairs, OpenMP over elements",
-            "cpu": cpu_model()}
+            "sample": f"median of {runs} timed runs of at least {min_seconds / runs:.1f} s, each "
+                      f"repeated evaluations of the whole {wl.name} workload ({wl.dof} DOF each); "
+                      f"the oracle's fp64 build, ordered pairs, OpenMP over elements",
+            "runs": rates, "cpu": cpu_model()}
 
 
 def main() -> int:

@@ -31,8 +31,8 @@ def check_f_plane(orc):
     assert np.array_equal(h[3], np.zeros_like(h[3]))
 
 
-def test_f_plane():
-    check_f_plane(oracle.default())
+def test_f_plane(orc):
+    check_f_plane(orc)
 
 
 def check_general_omega(orc):
@@ -45,8 +45,8 @@ def check_general_omega(orc):
     assert np.allclose(h[1:4], ref, rtol=1e-14, atol=1e-22)
 
 
-def test_general_omega():
-    check_general_omega(oracle.default())
+def test_general_omega(orc):
+    check_general_omega(orc)
 
 
 def check_entropy_with_rotation(orc, N):
@@ -66,5 +66,5 @@ def check_entropy_with_rotation(orc, N):
 
 
 @pytest.mark.parametrize("N", [2, 4])
-def test_entropy_with_rotation(N):
-    check_entropy_with_rotation(oracle.default(), N)
+def test_entropy_with_rotation(orc, N):
+    check_entropy_with_rotation(orc, N)

@@ -77,8 +77,8 @@ def check_global_entropy_conservation(orc, N, periodic, warp=0.05, seed=0):
 @pytest.mark.parametrize("N,periodic", [(1, (True, True, True)), (2, (True, True, True)),
                                         (3, (True, False, True)), (4, (False, False, False)),
                                         (7, (True, True, False))])
-def test_global_entropy_conservation(N, periodic):
-    check_global_entropy_conservation(oracle.default(), N, periodic)
+def test_global_entropy_conservation(orc, N, periodic):
+    check_global_entropy_conservation(orc, N, periodic)
 
 
 def test_surface_term_is_what_makes_entropy_vanish():
@@ -117,8 +117,8 @@ def check_conservation(orc, N, periodic, const_phi=False):
                                                   (3, (True, False, False), False),
                                                   (4, (True, True, True), True),
                                                   (2, (False, True, False), True)])
-def test_conservation(N, periodic, const_phi):
-    check_conservation(oracle.default(), N, periodic, const_phi)
+def test_conservation(orc, N, periodic, const_phi):
+    check_conservation(orc, N, periodic, const_phi)
 
 
 def check_free_stream_full(orc, N, periodic):
@@ -141,8 +141,8 @@ def check_free_stream_full(orc, N, periodic):
 
 @pytest.mark.parametrize("N,periodic", [(2, (True, True, True)), (4, (True, True, True)),
                                         (3, (True, False, False)), (7, (True, True, True))])
-def test_free_stream_full(N, periodic):
-    check_free_stream_full(oracle.default(), N, periodic)
+def test_free_stream_full(orc, N, periodic):
+    check_free_stream_full(orc, N, periodic)
 
 
 def check_hydrostatic_full(orc, N, warp):
@@ -169,8 +169,8 @@ def check_hydrostatic_full(orc, N, warp):
 
 
 @pytest.mark.parametrize("N,warp", [(2, 0.0), (3, 0.05), (4, 0.0), (4, 0.05), (7, 0.05)])
-def test_hydrostatic_full(N, warp):
-    check_hydrostatic_full(oracle.default(), N, warp)
+def test_hydrostatic_full(orc, N, warp):
+    check_hydrostatic_full(orc, N, warp)
 
 
 # --- 50-digit brute force of the surface term -------------------------------
@@ -246,8 +246,8 @@ def check_surface_vs_50_digits(orc, N):
 
 
 @pytest.mark.parametrize("N", [1, 2])
-def test_surface_vs_50_digits(N):
-    check_surface_vs_50_digits(oracle.default(), N)
+def test_surface_vs_50_digits(orc, N):
+    check_surface_vs_50_digits(orc, N)
 
 
 def test_surface_rejects_bad_neighbours():
