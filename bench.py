@@ -89,13 +89,31 @@ def counted_fp64_flops(workload: str, dtype: str):
     return fl + (measured_counter(workload, dtype, "fp64_trans_flops_per_launch") or 0.0)
 
 
+PREROLL_S = 0.25
+
+
+def preroll(run, sync, seconds: float = PREROLL_S) -> int:
+    """Untimed passes of `run()` until `seconds` of wall time have passed,
+    synchronising after each, so that the timed pass starts on a device that
+    has been busy (clocks up, caches and TLBs warm) however long the host
+    spent before it.  Returns the passes run."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        sync()
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False,
                   graph: bool = False):
     """Returns (seconds per step rotating cold buffers, seconds per step hot, info).
     With `full`, the whole right-hand side (volume + surface, esdg_rhs_*).
     With `graph`, the steps are captured once in a HIP graph (through torch's
     graph API) and the graph is replayed: the same launches without the
-    per-launch host overhead."""
+    per-launch host overhead.  Before each timed pass: `warmup` launches and
+    a pre-roll of at least PREROLL_S seconds (preroll())."""
     import torch
 
     from entropy_stable_dg_amd import esdg, inputs, perfmodel
@@ -134,10 +152,11 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
             if st != 0:
                 raise RuntimeError(esdg.esdg_status_string(st))
 
-    results = {}
+    results, prerolls = {}, {}
     for rotate in (True, False):
         run(warmup, rotate)
         torch.cuda.synchronize()
+        prerolls[rotate] = preroll(lambda: run(nsets, rotate), torch.cuda.synchronize)
         if graph:
             per_graph = min(steps, 100)
             g = torch.cuda.CUDAGraph()
@@ -173,6 +192,8 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
         log(f"{name}{' (graph replay)' if graph else ''}: {'rotating' if rotate else 'hot'} {results[rotate] * 1e6:.2f} us/step")
     info = dict(N=N, nelem=nelem, dof=wl.dof, dtype=dtype, description=wl.description,
                 seed=wl.seed, buffer_sets=nsets,
+                preroll={"seconds": PREROLL_S, "passes_rotating": prerolls[True],
+                         "passes_hot": prerolls[False], "launches_per_pass": nsets},
                 bytes=perfmodel.algorithmic_bytes(N, nelem, dtype),
                 flops=perfmodel.flops_per_element(N) * nelem)
     if full:
@@ -182,6 +203,109 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
     del sets
     torch.cuda.empty_cache()
     return results[True], results[False], info, wl
+
+
+# Time steps near the acoustic limit (0.5 x the smallest LGL node spacing over
+# the sound speed): bubble 62.5 m elements, N=4, smallest gap 10.8 m;
+# baroclinic 3.75 km tall elements, smallest vertical gap 650 m.
+STEP_DT = {"bubble": 7.0e-3, "bubble_f32": 7.0e-3, "baroclinic": 0.5, "baroclinic_f32": 0.5,
+           "tiny": 1.0e-4, "high_order": 2.0e-3}
+
+
+def time_stages(name: str, steps: int, warmup: int, rotate_bytes: float, pert: bool = False):
+    """Seconds per fused Runge-Kutta stage (whole right-hand side + the
+    low-storage update in one kernel, esdg_lsrk_steps_*), rotating over
+    enough independent states (> rotate_bytes) that no stage finds its inputs
+    in the cache.  Each timed call is two steps (ten stages, no final copy).
+    With `pert`, the state is carried as perturbation variables."""
+    import torch
+
+    from entropy_stable_dg_amd import esdg, inputs
+
+    if pert:
+        wl, qp, ref = inputs.make_perturbed(name)
+    else:
+        wl, qp, ref = inputs.make(name), None, None
+    dtype = "f32" if wl.q.dtype.name == "float32" else "f64"
+    dev = torch.device("cuda:0")
+    footprint = (3 * wl.q.nbytes + wl.phi.nbytes + wl.geom.nbytes
+                 + (ref.nbytes if ref is not None else 0))
+    nsets = max(2, math.ceil(rotate_bytes / footprint))
+    log(f"{name} stages{' (perturbation variables)' if pert else ''}: footprint "
+        f"{footprint / 1e6:.1f} MB x {nsets} sets")
+    sets = []
+    for _ in range(nsets):
+        q = torch.from_numpy(qp if pert else wl.q).to(dev)
+        sets.append(dict(q=q, q_tmp=torch.empty_like(q), dq=torch.empty_like(q),
+                         phi=torch.from_numpy(wl.phi).to(dev), geom=torch.from_numpy(wl.geom).to(dev),
+                         D=torch.from_numpy(wl.D).to(dev), nbr=torch.from_numpy(wl.nbr).to(dev),
+                         ref=torch.from_numpy(ref).to(dev) if pert else None))
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    fn = esdg.esdg_lsrk_steps_f64 if dtype == "f64" else esdg.esdg_lsrk_steps_f32
+    dt = STEP_DT[name]
+
+    def run(k: int) -> None:
+        for i in range(k):
+            t = sets[i % nsets]
+            st = fn(t["q"].data_ptr(), t["q_tmp"].data_ptr(), t["dq"].data_ptr(),
+                    t["ref"].data_ptr() if pert else None, t["phi"].data_ptr(),
+                    t["geom"].data_ptr(), t["D"].data_ptr(), t["nbr"].data_ptr(), None, dt, 2,
+                    wl.N, wl.nelem, handle)
+            if st != 0:
+                raise RuntimeError(esdg.esdg_status_string(st))
+
+    run(max(1, warmup // 10))
+    torch.cuda.synchronize()
+    passes = preroll(lambda: run(nsets), torch.cuda.synchronize)
+    calls = max(1, steps // 10)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    run(calls)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) * 1e-3 / (10 * calls)
+    finite = all(bool(torch.isfinite(t["q"]).all()) for t in sets)
+    log(f"{name} stage{' (perturbation variables)' if pert else ''}: {sec * 1e6:.2f} us/stage")
+    del sets
+    torch.cuda.empty_cache()
+    return sec, {"N": wl.N, "nelem": wl.nelem, "dof": wl.dof, "dtype": dtype, "dt": dt,
+                 "stages_timed": 10 * calls, "buffer_sets": nsets, "preroll_passes": passes,
+                 "state_finite_after": finite}
+
+
+def conservation_drift(name: str, nsteps: int, pert: bool = False) -> dict:
+    """Relative change of the sums of the integrals of rho, E and the entropy
+    over nsteps Runge-Kutta steps (esdg_integrals_* before and after
+    esdg_lsrk_steps_*): the global diagnostics of the page's baroclinic test."""
+    import numpy as np
+    import torch
+
+    from entropy_stable_dg_amd import esdg, inputs
+
+    if pert:
+        wl, qp, ref = inputs.make_perturbed(name)
+    else:
+        wl, qp, ref = inputs.make(name), None, None
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(qp if pert else wl.q).to(dev)
+    phi, geom, D, nbr = (torch.from_numpy(a).to(dev) for a in (wl.phi, wl.geom, wl.D, wl.nbr))
+    tref = torch.from_numpy(ref).to(dev) if pert else None
+    _, w = inputs.lgl(wl.N)
+    tw = torch.from_numpy(w.astype(wl.q.dtype)).to(dev)
+    before = esdg.integrals(q, phi, geom, tw, ref=tref).cpu().numpy()
+    dt = STEP_DT[name]
+    t0 = time.perf_counter()
+    esdg.lsrk_steps(q, phi, geom, D, nbr, dt, nsteps, ref=tref)
+    after = esdg.integrals(q, phi, geom, tw, ref=tref).cpu().numpy()
+    wall = time.perf_counter() - t0
+    rel = (after - before) / np.abs(before)
+    log(f"conservation {name}{' (perturbation variables)' if pert else ''}: {nsteps} steps of "
+        f"{dt} s: relative change mass {rel[0]:.2e} energy {rel[1]:.2e} entropy {rel[2]:.2e}")
+    return {"steps": nsteps, "dt": dt, "dtype": "f32" if wl.q.dtype.name == "float32" else "f64",
+            "perturbation_variables": pert, "relative_change_mass": float(rel[0]),
+            "relative_change_energy": float(rel[1]), "relative_change_entropy": float(rel[2]),
+            "initial": before.tolist(), "wall_s": wall}
 
 
 def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
@@ -432,6 +556,35 @@ def cpu_baseline(wl, min_seconds: float, runs: int = 3):
             "runs": rates, "cpu": cpu_model()}
 
 
+def roofline_of(achieved_gbs: float, gflops: float, stream_gbs: float, traffic):
+    """The roofline object of the dominant kernel, measured against whichever
+    roof this run comes closest to (HBM bytes, or fp64 vector FLOPs by the
+    analytic count: the kernel issues no MFMA), and a sentence naming what
+    binds, derived from the same figures: a roof binds when the kernel reaches
+    at least 70 % of it (of the measured stream for HBM), otherwise neither
+    does and the time goes to latency."""
+    from entropy_stable_dg_amd import perfmodel
+
+    hbm = achieved_gbs / perfmodel.PEAK_HBM_GBS
+    alu = gflops / (perfmodel.PEAK_FP64_VECTOR_TFLOPS * 1e3)
+    if hbm >= alu:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": perfmodel.PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": hbm, "traffic": traffic}
+    else:
+        roof = {"bound": "alu", "achieved": gflops / 1e3, "peak": perfmodel.PEAK_FP64_VECTOR_TFLOPS,
+                "unit": "TFLOP/s", "frac": alu, "traffic": traffic}
+    stream = achieved_gbs / stream_gbs
+    if stream >= 0.7:
+        what = "HBM binds"
+    elif alu >= 0.7:
+        what = "the fp64 vector units bind"
+    else:
+        what = "neither roof binds: latency (the load phase of each workgroup round) takes the rest"
+    sentence = (f"{what}: {100 * hbm:.0f} % of nominal HBM ({100 * stream:.0f} % of the measured "
+                f"8:1 stream), {100 * alu:.0f} % of the fp64 vector peak by the analytic count")
+    return roof, sentence
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,6 +603,11 @@ def main() -> int:
                     help="comma-separated extra workloads to time (reported under 'extra'); "
                          "a ':rhs' suffix times the whole right-hand side (volume + surface), "
                          "':graph' replays the launches from a captured HIP graph")
+    ap.add_argument("--stages", default="bubble,bubble_f32,bubble_f32:pert",
+                    help="workloads whose fused Runge-Kutta stage (whole rhs + update) is timed "
+                         "(reported under 'stage'); ':pert' for perturbation variables")
+    ap.add_argument("--conservation-steps", type=int, default=500,
+                    help="steps of the conservation-drift diagnostics (0: none)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
     ap.add_argument("--ablation-steps", type=int, default=10)
@@ -530,6 +688,24 @@ def main() -> int:
                 and inf["nelem"] == info["nelem"]):
             extra[key]["speedup_over_fp64"] = (inf["dof"] / c) / value
 
+    stage = {}
+    for key in [x for x in args.stages.split(",") if x]:
+        name, _, mode = key.partition(":")
+        sec, inf = time_stages(name, args.steps, args.warmup, args.rotate_mb * 1e6, pert=(mode == "pert"))
+        stage[key] = dict(inf, us_per_stage=sec * 1e6, dof_stage_updates_per_s=inf["dof"] / sec,
+                          what="one fused launch: whole right-hand side (volume + surface) and the "
+                               "low-storage Runge-Kutta update of the register and the state")
+    if "bubble" in stage and "bubble_f32" in stage:
+        stage["bubble_f32"]["speedup_over_fp64"] = (stage["bubble"]["us_per_stage"]
+                                                    / stage["bubble_f32"]["us_per_stage"])
+
+    conservation = {}
+    if args.conservation_steps > 0:
+        for key in ("bubble", "bubble_f32", "bubble_f32:pert", "baroclinic", "baroclinic_f32",
+                    "baroclinic_f32:pert"):
+            name, _, mode = key.partition(":")
+            conservation[key] = conservation_drift(name, args.conservation_steps, pert=(mode == "pert"))
+
     ablation = None
     if not args.no_ablation:
         ablation = time_ablation(args.ablation_steps, 2)
@@ -540,6 +716,8 @@ def main() -> int:
     stream_gbs = max(stream_narrow, stream_wide)
     log(f"HBM stream probe (8 reads : 1 write, fp64): {stream_narrow:.0f} GB/s with 8-byte lanes, "
         f"{stream_wide:.0f} GB/s with 32-byte lanes")
+
+    roofline, binding = roofline_of(achieved_gbs, gflops, stream_gbs, traffic)
 
     cpu = None
     cpu1 = None
@@ -566,14 +744,7 @@ def main() -> int:
             "N": info["N"], "nelem": info["nelem"], "dof": info["dof"], "seed": info["seed"],
             "buffer_sets": info["buffer_sets"], "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved_gbs,
-            "peak": perfmodel.PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / perfmodel.PEAK_HBM_GBS,
-            "traffic": traffic,
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "gflops_analytic_fp64": gflops,
         "frac_fp64_vector_peak": gflops / (perfmodel.PEAK_FP64_VECTOR_TFLOPS * 1e3),
@@ -583,8 +754,7 @@ def main() -> int:
         "frac_fp64_vector_peak_counted": (counted_flops / t_cold / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                           if counted_flops else None),
         "hbm_gbs_counted": traffic / t_cold / 1e9 if traffic else None,
-        "binding_roof": "HBM at scale (about 91 % of the measured stream at 262,144 elements); at this "
-                        "size the first round of workgroups' loads cannot overlap compute",
+        "binding_roof": binding,
         "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
         "hot_ms_per_step": t_hot * 1e3,
         "hot_dof_per_s": info["dof"] / t_hot,
@@ -594,6 +764,8 @@ def main() -> int:
         "frac_of_measured_stream": achieved_gbs / stream_gbs,
         "cpu_oracle_one_core": cpu1,
         "extra": extra,
+        "stage": stage,
+        "conservation": conservation,
         "ablation": ablation,
     }
     print(json.dumps(out), flush=True)

@@ -460,16 +460,18 @@ struct LineTask {
 };
 
 // Global values one thread loads for phase A: IT nodes x (5 fields, phi,
-// 9 metric terms when staged, J).
-template <typename T, int N, class C>
+// with PERT the reference density and pressure, 9 metric terms when staged,
+// J).
+template <typename T, int N, class C, bool PERT = false>
 struct NodeLoads {
     using S = Shape<N, C>;
     static constexpr int IT = S::kNodeIters;
-    T v[IT][6];
+    T v[IT][PERT ? 8 : 6];
     T m[C::kMetricInLds ? IT : 1][9];
     T J[IT];
-    __device__ inline void issue(const T *__restrict__ q, const T *__restrict__ phi,
-                                 const T *__restrict__ geom, int64_t fstride, const Batch<N, C> &B) {
+    __device__ inline void issue(const T *__restrict__ q, const T *__restrict__ ref,
+                                 const T *__restrict__ phi, const T *__restrict__ geom,
+                                 int64_t fstride, const Batch<N, C> &B) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int t = threadIdx.x + it * C::NT;
@@ -478,6 +480,10 @@ struct NodeLoads {
 #pragma unroll
                 for (int f = 0; f < 5; ++f) v[it][f] = q[f * fstride + g];
                 v[it][5] = phi[g];
+                if constexpr (PERT) {
+                    v[it][6] = ref[g];
+                    v[it][7] = ref[fstride + g];
+                }
                 if constexpr (C::kMetricInLds) {
 #pragma unroll
                     for (int j = 0; j < 9; ++j) m[it][j] = geom[j * fstride + g];
@@ -493,13 +499,24 @@ struct NodeLoads {
 // the surface term builds them for the face partners in a neighbouring
 // element with the same operations, so both sides of a face see identical
 // values.
-template <typename T>
-__device__ inline NodeRegs<T> node_values(T rho, T m1, T m2, T m3, T E, T ph)
+//
+// With PERT the state is carried as perturbation variables about a reference
+// at rest with density rbar and pressure pbar (total energy
+// Ebar = pbar/(gamma-1) + rbar phi): r = rho - rbar, E = E_full - Ebar, the
+// momentum unchanged.  Then rho = rbar + r and
+//     p = pbar + (gamma-1)(E - |m|^2/(2 rho) - r phi),
+// the same pressure law with the reference's share taken out before the
+// subtraction, so the small differences are formed without the large
+// reference values.
+template <typename T, bool PERT = false>
+__device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rbar = T(0),
+                                          T pbar = T(0))
 {
     using A = Arith<T>;
     const T gm1 = T(kGamma - 1.0);
     const T bscale = T(kBScale);
     NodeRegs<T> V;
+    const T rho = PERT ? rbar + r : r;
     const T irho = A::rcp(rho);
     const T hirho = T(0.5) * irho;
     V.rho = rho;
@@ -507,7 +524,8 @@ __device__ inline NodeRegs<T> node_values(T rho, T m1, T m2, T m3, T E, T ph)
     V.u2 = m2 * hirho;
     V.u3 = m3 * hirho;
     const T usq4 = V.u1 * V.u1 + V.u2 * V.u2 + V.u3 * V.u3;  // |u|^2 / 4
-    const T p = gm1 * (E - (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - rho * ph);
+    const T dE = E - (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - r * ph;
+    const T p = PERT ? fma(gm1, dE, pbar) : gm1 * dE;
     V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
     V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
     V.lrho = A::node_log(rho);
@@ -518,9 +536,9 @@ __device__ inline NodeRegs<T> node_values(T rho, T m1, T m2, T m3, T E, T ph)
 }
 
 // Phase A compute: per-node primitives and logs into LDS; returns -1/J per node.
-template <typename T, int N, class C>
-__device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C> &B, T *lds,
-                                   T (&mJ)[Shape<N, C>::kNodeIters])
+template <typename T, int N, class C, bool PERT>
+__device__ inline void stage_nodes(const NodeLoads<T, N, C, PERT> &L, const Batch<N, C> &B,
+                                   T *lds, T (&mJ)[Shape<N, C>::kNodeIters])
 {
     using A = Arith<T>;
     constexpr int SLOTS = Shape<N, C>::kSlots;
@@ -529,8 +547,13 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
             const int st = Shape<N, C>::slot(t);
-            const NodeRegs<T> V = node_values(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
-                                              L.v[it][4], L.v[it][5]);
+            NodeRegs<T> V;
+            if constexpr (PERT)
+                V = node_values<T, true>(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
+                                         L.v[it][4], L.v[it][5], L.v[it][6], L.v[it][7]);
+            else
+                V = node_values(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3], L.v[it][4],
+                                L.v[it][5]);
             lds[kRho * SLOTS + st] = V.rho;
             lds[kU1 * SLOTS + st] = V.u1;
             lds[kU2 * SLOTS + st] = V.u2;
@@ -562,10 +585,10 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C> &L, const Batch<N, C
 // node (velocity reflected in the face normal Ja^k).
 constexpr int32_t kFaceWall = -1;
 
-template <typename T>
+template <typename T, bool PERT = false>
 struct FaceLoads {
     int32_t nb[2];   // neighbour across the face at line end 0 (a = 0) and end 1 (a = N)
-    T v[2][6];       // its matching node: 5 conserved fields and phi
+    T v[2][PERT ? 8 : 6];  // its matching node: 5 conserved fields, phi (and the reference)
     __device__ inline void issue_neighbours(const int32_t *__restrict__ nbr, int64_t e, int k) {
         nb[0] = nbr[6 * e + 2 * k];
         nb[1] = nbr[6 * e + 2 * k + 1];
@@ -574,8 +597,9 @@ struct FaceLoads {
     // its element, `step` the node stride along the line.  Indices outside
     // [0, nelem) load nothing.
     template <int N>
-    __device__ inline void issue_states(const T *__restrict__ q, const T *__restrict__ phi,
-                                        int64_t fstride, int64_t nelem, int local0, int step) {
+    __device__ inline void issue_states(const T *__restrict__ q, const T *__restrict__ ref,
+                                        const T *__restrict__ phi, int64_t fstride, int64_t nelem,
+                                        int local0, int step) {
         constexpr int Np = (N + 1) * (N + 1) * (N + 1);
 #pragma unroll
         for (int end = 0; end < 2; ++end) {
@@ -584,15 +608,27 @@ struct FaceLoads {
 #pragma unroll
                 for (int f = 0; f < 5; ++f) v[end][f] = q[f * fstride + g];
                 v[end][5] = phi[g];
+                if constexpr (PERT) {
+                    v[end][6] = ref[g];
+                    v[end][7] = ref[fstride + g];
+                }
             }
         }
     }
+    __device__ inline NodeRegs<T> partner(int end) const {
+        if constexpr (PERT)
+            return node_values<T, true>(v[end][0], v[end][1], v[end][2], v[end][3], v[end][4],
+                                        v[end][5], v[end][6], v[end][7]);
+        else
+            return node_values(v[end][0], v[end][1], v[end][2], v[end][3], v[end][4], v[end][5]);
+    }
 };
 
-template <typename T, int N, class C>
+template <typename T, int N, class C, bool PERT>
 __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
                                     const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
-                                    const FaceLoads<T> &F, int64_t nelem, T (&acc)[N + 1][5])
+                                    const FaceLoads<T, PERT> &F, int64_t nelem,
+                                    T (&acc)[N + 1][5])
 {
     using A = Arith<T>;
     constexpr int SLOTS = Shape<N, C>::kSlots;
@@ -620,8 +656,7 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
             Y.u2 = X.u2 - un2 * X.n2;
             Y.u3 = X.u3 - un2 * X.n3;
         } else if (nb >= 0 && nb < nelem) {
-            Y = node_values(F.v[end][0], F.v[end][1], F.v[end][2], F.v[end][3], F.v[end][4],
-                            F.v[end][5]);
+            Y = F.partner(end);
             Y.n1 = X.n1; Y.n2 = X.n2; Y.n3 = X.n3;
         } else {
             Y.rho = T(__builtin_nan(""));  // invalid neighbour index: the result says so
@@ -732,12 +767,52 @@ template <typename T>
 struct Rotation {
     T w1, w2, w3;
     bool on;
-    __device__ inline void add(const T *__restrict__ q, int64_t fstride, int64_t g,
-                               T &h1, T &h2, T &h3) const {
-        const T U1 = q[fstride + g], U2 = q[2 * fstride + g], U3 = q[3 * fstride + g];
+    __device__ inline void add(T U1, T U2, T U3, T &h1, T &h2, T &h3) const {
         h1 -= w2 * U3 - w3 * U2;
         h2 -= w3 * U1 - w1 * U3;
         h3 -= w1 * U2 - w2 * U1;
+    }
+};
+
+// Where a node's right-hand side r goes.  Without STAGE it is stored as is.
+// With STAGE the kernel is one stage of a 2N-storage low-storage Runge-Kutta
+// scheme ([ESDG-GPU §3] steps with such a scheme and recomputes the fluxes
+// at every stage), fused into the store:
+//     dq <- a dq + dt r,    q_out <- q + b dq,
+// with `out` the register dq and q the stage's input state (perturbation
+// variables with PERT: the reference is fixed in time).  a == 0 does not
+// read dq (the first stage may find it uninitialised).  The source term is
+// added to r before the update.
+template <typename T, bool STAGE>
+struct Sink {
+    T *__restrict__ out;    // rhs, or the register dq with STAGE
+    T *__restrict__ q_out;  // STAGE: the stage's output state
+    T a, b, dt;             // STAGE: the stage's coefficients and the step
+    __device__ inline void put(const T *__restrict__ q, int64_t fstride, int64_t g,
+                               const Rotation<T> &rot, T (&r)[5]) const {
+        T U[5];
+        if (STAGE || rot.on) {
+#pragma unroll
+            for (int f = STAGE ? 0 : 1; f < (STAGE ? 5 : 4); ++f) U[f] = q[f * fstride + g];
+        }
+        if (rot.on) rot.add(U[1], U[2], U[3], r[1], r[2], r[3]);
+        if constexpr (STAGE) {
+            T k[5];
+#pragma unroll
+            for (int f = 0; f < 5; ++f) k[f] = dt * r[f];
+            if (a != T(0)) {
+#pragma unroll
+                for (int f = 0; f < 5; ++f) k[f] = fma(a, out[f * fstride + g], k[f]);
+            }
+#pragma unroll
+            for (int f = 0; f < 5; ++f) {
+                out[f * fstride + g] = k[f];
+                q_out[f * fstride + g] = fma(b, k[f], U[f]);
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 5; ++f) out[f * fstride + g] = r[f];
+        }
     }
 };
 
@@ -759,11 +834,11 @@ __device__ inline void write_partials(T *lds, const LineTask<N, C> &L, bool acti
 
 // FIN: a direction-3 line thread adds the direction-1 and -2 partials of its
 // nodes to its own (same order as store_rhs), scales by -1/J and stores.
-template <typename T, int N, class C>
+template <typename T, int N, class C, bool STAGE>
 __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool active,
                                    const Batch<N, C> &B, int64_t fstride,
                                    const T (&acc)[N + 1][5], const T *__restrict__ q,
-                                   const Rotation<T> &rot, T *__restrict__ rhs)
+                                   const Rotation<T> &rot, const Sink<T, STAGE> &sink)
 {
     constexpr int SLOTS = Shape<N, C>::kSlots;
     if (active && L.k == 2) {
@@ -776,17 +851,15 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
 #pragma unroll
             for (int f = 0; f < 5; ++f)
                 r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + acc[a][f]) * mJ;
-            if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
-#pragma unroll
-            for (int f = 0; f < 5; ++f) rhs[f * fstride + g] = r[f];
+            sink.put(q, fstride, g, rot, r);
         }
     }
 }
 
-template <typename T, int N, class C>
+template <typename T, int N, class C, bool STAGE>
 __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fstride,
                                  const T (&mJ)[Shape<N, C>::kNodeIters], const T *__restrict__ q,
-                                 const Rotation<T> &rot, T *__restrict__ rhs)
+                                 const Rotation<T> &rot, const Sink<T, STAGE> &sink)
 {
     constexpr int SLOTS = Shape<N, C>::kSlots;
 #pragma unroll
@@ -801,24 +874,26 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
                 const T s = lds[f * SLOTS + st] + lds[(5 + f) * SLOTS + st] + lds[(10 + f) * SLOTS + st];
                 r[f] = s * mJ[it];
             }
-            if (rot.on) rot.add(q, fstride, g, r[1], r[2], r[3]);
-#pragma unroll
-            for (int f = 0; f < 5; ++f) rhs[f * fstride + g] = r[f];
+            sink.put(q, fstride, g, rot, r);
         }
     }
 }
 
 // One workgroup per batch of EPB elements.  SURF adds the entropy-conservative
 // surface term (face neighbours from nbr), giving the whole right-hand side;
-// rot.on adds the Coriolis source.
-template <typename T, int N, class C, bool SURF = false>
+// rot.on adds the Coriolis source.  STAGE fuses a Runge-Kutta stage into the
+// store (Sink); PERT reads the state as perturbation variables about the
+// reference ref = (rbar, pbar) (node_values).
+template <typename T, int N, class C, bool SURF = false, bool STAGE = false, bool PERT = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
 __attribute__((amdgpu_waves_per_eu(SURF ? (C::WAVES_SURF > 0 ? C::WAVES_SURF : 1)
                                          : (C::WAVES > 0 ? C::WAVES : 1))))
-volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *__restrict__ geom,
-                  const T *__restrict__ D, const int32_t *__restrict__ nbr, Rotation<T> rot,
-                  int64_t nelem, T *__restrict__ rhs)
+volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *__restrict__ phi,
+                  const T *__restrict__ geom, const T *__restrict__ D,
+                  const int32_t *__restrict__ nbr, Rotation<T> rot, int64_t nelem,
+                  Sink<T, STAGE> sink)
 {
+    static_assert(SURF || !(STAGE || PERT), "stages and perturbation variables need the whole rhs");
     using S = Shape<N, C>;
     constexpr int Nq = N + 1;
     __shared__ T lds[S::kLdsValues];
@@ -831,12 +906,12 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     if constexpr (!SURF) rot.on = false;  // the volume term alone has no source
 
     // phase A: issue every global load first
-    FaceLoads<T> face;
+    FaceLoads<T, PERT> face;
     if constexpr (SURF) {
         if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
     }
-    NodeLoads<T, N, C> ld;
-    ld.issue(q, phi, geom, fstride, B);
+    NodeLoads<T, N, C, PERT> ld;
+    ld.issue(q, ref, phi, geom, fstride, B);
     T lm[C::kMetricInLds ? 1 : Nq][3];
     if constexpr (!C::kMetricInLds) {
         if (active) {
@@ -848,11 +923,11 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
         }
     }
     if constexpr (SURF) {
-        if (active) face.template issue_states<N>(q, phi, fstride, nelem, L.first_in_element(),
-                                                     L.node_step());
+        if (active) face.template issue_states<N>(q, ref, phi, fstride, nelem,
+                                                     L.first_in_element(), L.node_step());
     }
     T mJ[S::kNodeIters];
-    stage_nodes<T, N, C>(ld, B, lds, mJ);
+    stage_nodes<T, N, C, PERT>(ld, B, lds, mJ);
     __syncthreads();
 
     // phase B
@@ -863,7 +938,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
         for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
     // the face partners first: their loaded states die before the pair loop
     if constexpr (SURF) {
-        if (active) surface_ends<T, N, C>(lds, L, lm, face, nelem, acc);
+        if (active) surface_ends<T, N, C, PERT>(lds, L, lm, face, nelem, acc);
     }
     constexpr bool kSplit = SURF ? C::kSeriesFormSurf : C::kSeriesForm;
     if (active) line_pairs<T, N, C, kSplit>(lds, D, L, lm, acc);
@@ -873,9 +948,9 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ phi, const T *_
     write_partials<T, N, C>(lds, L, active, acc);
     __syncthreads();
     if constexpr (C::kFinalizeInLine) {
-        finish_line<T, N, C>(lds, L, active, B, fstride, acc, q, rot, rhs);
+        finish_line<T, N, C, STAGE>(lds, L, active, B, fstride, acc, q, rot, sink);
     } else {
-        store_rhs<T, N, C>(lds, B, fstride, mJ, q, rot, rhs);
+        store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
     }
 }
 

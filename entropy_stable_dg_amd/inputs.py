@@ -247,6 +247,28 @@ def state_channel(X, L, T0=300.0, T_noise=1.0, u_max=35.0, rng=None):
     return conserved(rho, u, p, phi), phi
 
 
+def reference_at_rest(state: str, X, theta0=300.0, T0=300.0):
+    """The hydrostatic state at rest a workload's perturbation variables are
+    taken about: the isentropic base of the bubble (without the bubble), the
+    isothermal base of the other states.  Returns (rbar, pbar) shaped like
+    X[0]."""
+    z = X[2]
+    phi = GRAV * z
+    if state == "bubble":
+        pi_ex = 1.0 - GRAV * z / (CP * theta0)
+        p = P0 * pi_ex ** (CP / R_GAS)
+        return p / (R_GAS * theta0 * pi_ex), p
+    p = P0 * np.exp(-phi / (R_GAS * T0))
+    return p / (R_GAS * T0), p
+
+
+def perturbation_variables(q, phi, rbar, pbar):
+    """q' = q - qbar with qbar = (rbar, 0, 0, 0, pbar/(gamma-1) + rbar phi),
+    the reference at rest (fp64)."""
+    qbar = conserved(rbar, np.zeros((3,) + np.shape(rbar)), pbar, phi)
+    return q - qbar
+
+
 # ---------------------------------------------------------------------------
 # Named workloads
 # ---------------------------------------------------------------------------
@@ -352,6 +374,10 @@ CONFIGS = {
                        description="80x16x8 hexes on a 40000x6000x30 km channel, N=4, "
                                    "isothermal 300 K base + U(-1,1) K noise, zonal jet 35 m/s, "
                                    "seeded sinusoidal warp of 5% of the element size"),
+    "baroclinic_f32": dict(K=(80, 16, 8), lo=(0, 0, 0), hi=(4.0e7, 6.0e6, 3.0e4), N=4,
+                           state="channel", seed=303, warp_frac=0.05, dtype="f32",
+                           periodic=(True, False, False),
+                           description="the baroclinic-channel workload rounded to fp32"),
     "bubble_f32": dict(K=(16, 16, 16), lo=(0, 0, 0), hi=(1000, 1000, 1000), N=4, state="bubble",
                        seed=202, dtype="f32", periodic=(True, True, False),
                        description="the rising-bubble workload rounded to fp32"),
@@ -367,6 +393,25 @@ def make(name: str, **override) -> Workload:
     cfg = dict(CONFIGS[name])
     cfg.update(override)
     return build_workload(name, **cfg)
+
+
+def make_perturbed(name: str, **override):
+    """A named workload with its state as perturbation variables about its
+    reference at rest (reference_at_rest).  Returns (wl, qp, ref): wl as
+    make() returns it, qp [5][nelem][Np] and ref [2][nelem][Np] (rbar, pbar)
+    in the workload's dtype, qp formed in fp64 from the fp64 state before
+    rounding."""
+    cfg = dict(CONFIGS[name])
+    cfg.update(override)
+    dtype = cfg.get("dtype", "f64")
+    wl64 = build_workload(name, **dict(cfg, dtype="f64"))
+    X = wl64.X
+    rbar, pbar = reference_at_rest(cfg["state"], X)
+    qp = perturbation_variables(wl64.q, wl64.phi, rbar, pbar)
+    ref = np.stack([rbar, pbar])
+    wl = wl64 if dtype == "f64" else build_workload(name, **cfg)
+    npdt = np.float64 if dtype == "f64" else np.float32
+    return wl, np.ascontiguousarray(qp.astype(npdt)), np.ascontiguousarray(ref.astype(npdt))
 
 
 def dof_count(N: int, K=(1, 1, 1), L: int = 0) -> int:

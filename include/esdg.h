@@ -1,8 +1,11 @@
 /*
  * esdg.h -- C ABI of the ESDG flux-differencing volume-term library
  * (libesdg.so, HIP for AMD gfx950): the volume term alone
- * (esdg_volume_rhs_*) and the whole right-hand side with the
- * entropy-conservative surface term fused into the same kernel (esdg_rhs_*).
+ * (esdg_volume_rhs_*), the whole right-hand side with the
+ * entropy-conservative surface term fused into the same kernel (esdg_rhs_*,
+ * esdg_rhs_pert_* for perturbation variables), low-storage Runge-Kutta
+ * stages and steps with the right-hand side fused in (esdg_lsrk_*), and the
+ * global conservation integrals (esdg_integrals_*).
  *
  * The operation is the volume term of the semi-discrete entropy-stable DG
  * form of "GPU Performance of an Entropy-Stable Discontinuous Galerkin Euler
@@ -56,7 +59,7 @@ extern "C" {
 #define ESDG_ERR_ORDER  (-2)  /* N outside [esdg_min_order(), esdg_max_order()]     */
 #define ESDG_ERR_NELEM  (-3)  /* nelem < 0, or the arrays would not be addressable  */
 #define ESDG_ERR_LAUNCH (-4)  /* the kernel launch failed (hipGetLastError)         */
-#define ESDG_ERR_ALIAS  (-5)  /* rhs overlaps an input array                        */
+#define ESDG_ERR_ALIAS  (-5)  /* an output overlaps an input or another output      */
 
 /* Volume term in fp64 arithmetic. Returns a status code above. */
 int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom,
@@ -105,6 +108,117 @@ int esdg_rhs_f64(const double *q, const double *phi, const double *geom,
 int esdg_rhs_f32(const float *q, const float *phi, const float *geom,
                  const float *D, const int32_t *nbr, const float *omega, int N,
                  int64_t nelem, float *rhs, hipStream_t stream);
+
+/*
+ * Whole right-hand side (as esdg_rhs_*) of a state carried in perturbation
+ * variables about a reference state at rest, the cure the page names for the
+ * noise of 32-bit runs on full state variables ([ESDG-GPU §5.2], the last
+ * paragraph of the baroclinic test).  With the reference's density rbar and
+ * pressure pbar (its total energy Ebar = pbar/(gamma-1) + rbar phi):
+ *
+ *   qp   [5][nelem][Np]  rho - rbar, rho u1, rho u2, rho u3, E - Ebar
+ *   ref  [2][nelem][Np]  rbar, pbar (> 0)
+ *
+ * and the result is the right-hand side of the full state
+ * (rbar + qp0, qp1, qp2, qp3, Ebar + qp4).  The kernel forms the pressure as
+ * pbar + (gamma-1)(qp4 - |U|^2/(2 rho) - qp0 phi), so the reference's share
+ * never enters the subtraction.  rhs must not overlap ref either; ref == NULL
+ * gives ESDG_ERR_NULL.  Everything else as esdg_rhs_f64.
+ */
+int esdg_rhs_pert_f64(const double *qp, const double *ref, const double *phi, const double *geom,
+                      const double *D, const int32_t *nbr, const double *omega, int N,
+                      int64_t nelem, double *rhs, hipStream_t stream);
+int esdg_rhs_pert_f32(const float *qp, const float *ref, const float *phi, const float *geom,
+                      const float *D, const int32_t *nbr, const float *omega, int N,
+                      int64_t nelem, float *rhs, hipStream_t stream);
+
+/*
+ * One stage of a 2N-storage low-storage Runge-Kutta scheme on the whole
+ * right-hand side L (as esdg_rhs_*, or esdg_rhs_pert_* when ref is given),
+ * fused into the same kernel ([ESDG-GPU §3]: the solver advances with a
+ * low-storage Runge-Kutta scheme and recomputes the fluxes at every stage;
+ * [ESDG-GPU §4.2, Fig. 4] times the update as a kernel of its own):
+ *
+ *   dq    <- a dq + dt L(q_in)          (a == 0: dq is not read)
+ *   q_out <- q_in + b dq
+ *
+ *   q_in   [5][nelem][Np]  the stage's state (perturbation variables with ref)
+ *   ref    [2][nelem][Np]  or NULL: reference density and pressure, as above
+ *   dq     [5][nelem][Np]  the scheme's register, read (a != 0) and written
+ *   q_out  [5][nelem][Np]  OUTPUT: the next stage's state
+ *
+ * q_out and dq must not overlap each other or any input (q_out cannot be
+ * q_in: neighbouring elements read q_in's face nodes during the launch);
+ * ESDG_ERR_ALIAS otherwise.  nbr, omega and the rest as esdg_rhs_f64.
+ */
+int esdg_lsrk_stage_f64(const double *q_in, const double *ref, const double *phi,
+                        const double *geom, const double *D, const int32_t *nbr,
+                        const double *omega, double a, double b, double dt, int N, int64_t nelem,
+                        double *dq, double *q_out, hipStream_t stream);
+int esdg_lsrk_stage_f32(const float *q_in, const float *ref, const float *phi, const float *geom,
+                        const float *D, const int32_t *nbr, const float *omega, float a, float b,
+                        float dt, int N, int64_t nelem, float *dq, float *q_out,
+                        hipStream_t stream);
+
+/*
+ * nsteps >= 0 steps of size dt of dq/dt = L(q) (the whole right-hand side,
+ * in perturbation variables when ref is given) with the five-stage
+ * fourth-order 2N-storage scheme of Carpenter and Kennedy (1994), which
+ * stands in for the page's fourteen-stage scheme (its coefficients are not
+ * on the page; the page's solver used a five-stage fourth-order scheme
+ * before).  The stages ping-pong between q and q_tmp; the result is left in
+ * q (one device copy at the end when the stage count is odd).
+ *
+ *   q      [5][nelem][Np]  in: the state; out: the state after nsteps steps
+ *   q_tmp  [5][nelem][Np]  workspace, overwritten
+ *   dq     [5][nelem][Np]  workspace (the register), overwritten
+ *
+ * q, q_tmp and dq must be pairwise disjoint and disjoint from the inputs
+ * (ESDG_ERR_ALIAS); nsteps < 0 gives ESDG_ERR_NELEM; nsteps == 0 or
+ * nelem == 0 is a no-op.  Launches 5 nsteps kernels (+1 copy) on `stream`
+ * and returns at once; an error from a later launch stops the sequence and
+ * is returned.
+ */
+int esdg_lsrk_steps_f64(double *q, double *q_tmp, double *dq, const double *ref,
+                        const double *phi, const double *geom, const double *D,
+                        const int32_t *nbr, const double *omega, double dt, int nsteps, int N,
+                        int64_t nelem, hipStream_t stream);
+int esdg_lsrk_steps_f32(float *q, float *q_tmp, float *dq, const float *ref, const float *phi,
+                        const float *geom, const float *D, const int32_t *nbr,
+                        const float *omega, float dt, int nsteps, int N, int64_t nelem,
+                        hipStream_t stream);
+
+/* Stage count of the scheme esdg_lsrk_steps_* uses (5), and its coefficients:
+ * stage s updates dq <- A[s] dq + dt L(q), q <- q + B[s] dq.  A and B are HOST
+ * arrays of esdg_lsrk_stages() doubles; returns ESDG_ERR_NULL if either is
+ * NULL. */
+int esdg_lsrk_stages(void);
+int esdg_lsrk_coefficients(double *A, double *B);
+
+/*
+ * Global conservation diagnostics of [ESDG-GPU §5.2]: the sums over the
+ * elements of the integrals of rho, of E (= rho e, e including phi) and of
+ * the entropy eta = -rho s/(gamma-1), s = ln p - gamma ln rho, by the LGL
+ * quadrature of the collocation nodes (weight w[a] w[b] w[c] J at node
+ * a + Nq (b + Nq c)).
+ *
+ *   q, ref, phi, geom  as above (ref NULL: q is the full state)
+ *   w      [Nq]        device: the LGL quadrature weights on [-1, 1]
+ *   work   device workspace of esdg_integrals_workspace_bytes() bytes
+ *   out    device, 3 doubles: OUTPUT (integral of rho, of E, of eta)
+ *
+ * Every node's terms are formed and summed in fp64 (also for the fp32 entry);
+ * the sum is deterministic (fixed partition and reduction order for a given
+ * nelem and N).  nelem == 0 writes zeros.  work and out must not overlap each
+ * other or an input (ESDG_ERR_ALIAS).
+ */
+int64_t esdg_integrals_workspace_bytes(void);
+int esdg_integrals_f64(const double *q, const double *ref, const double *phi, const double *geom,
+                       const double *w, int N, int64_t nelem, double *work, double *out,
+                       hipStream_t stream);
+int esdg_integrals_f32(const float *q, const float *ref, const float *phi, const float *geom,
+                       const float *w, int N, int64_t nelem, double *work, double *out,
+                       hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *esdg_status_string(int status);

@@ -1,0 +1,314 @@
+"""GPU parity of the time stepping (fused Runge-Kutta stages, esdg_lsrk_*),
+the whole right-hand side in perturbation variables (esdg_rhs_pert_*) and
+the conservation integrals (esdg_integrals_*) against the CPU oracle.
+
+Tolerance of a stepped state.  After K steps the state is
+q_K = q_0 + sum over the stages of (weight) dt L(q_s); with the stage weights
+summing to one in magnitude, the right-hand side's own bar (error over the
+largest summand magnitude, 1e-11 fp64 / 2e-5 fp32) carries over as
+K dt tol max mag, and storing the state after each of the 5K stages rounds
+it by at most half an ulp of the stored variable.  So, per field,
+
+    max |q_gpu - q_oracle| <= 2 (K dt tol max_i mag_i + 5K eps max |stored|)
+
+with mag the oracle's summed magnitudes at q_0, eps the unit roundoff of the
+working precision and `stored` the state the kernels update (the full state,
+or the perturbation variables about the reference).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from entropy_stable_dg_amd import esdg
+from entropy_stable_dg_amd import inputs as I
+from tests.test_gpu_parity import dev, to_gpu
+from tests.test_gpu_rhs import random_closed_mesh
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float64: 1e-11, np.float32: 2e-5}
+EPS = {np.float64: 2.0 ** -53, np.float32: 2.0 ** -24}
+
+
+def gpu_steps(q, phi, geom, D, nbr, dt, K, ref=None, omega=None):
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    tn = torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev())
+    tr = to_gpu(ref)[0] if ref is not None else None
+    esdg.lsrk_steps(tq, tp, tg, tD, tn, dt, K, ref=tr, omega=omega)
+    torch.cuda.synchronize()
+    return tq.cpu().numpy()
+
+
+def stepped_check(got, q0, phi, geom, D, nbr, N, dt, K, dtype, ref=None, omega=None, label=""):
+    """Compare a GPU-stepped state with the oracle's K steps from the same
+    (promoted) initial state; returns the per-field errors over the bound."""
+    full0 = q0 if ref is None else oracle.full_state(q0, ref, phi)
+    want = oracle.lsrk(full0, phi, geom, D, nbr, N, dt, K, omega=omega)
+    _, mag = oracle.rhs(full0, phi, geom, D, nbr, N, omega=omega, with_magnitude=True)
+    got_full = got.astype(np.float64) if ref is None else oracle.full_state(got, ref, phi)
+    stored = q0 if ref is None else got
+    ratios = []
+    for f in range(5):
+        err = np.abs(got_full[f] - want[f]).max()
+        bound = 2 * (K * dt * TOL[dtype] * np.abs(mag[f]).max()
+                     + 5 * K * EPS[dtype] * np.abs(stored[f].astype(np.float64)).max())
+        ratios.append(err / bound)
+    moved = [float(np.abs(want[f] - full0[f]).max()) for f in range(5)]
+    print(f"[time] {label}: error/bound per field {['%.2e' % r for r in ratios]}; "
+          f"max |q_K - q_0| {['%.2e' % m for m in moved]}", flush=True)
+    assert np.all(np.isfinite(got)), label
+    assert max(ratios) <= 1.0, (label, ratios)
+    return ratios
+
+
+def perturbed(q, phi, X, state="isothermal"):
+    rbar, pbar = I.reference_at_rest(state, X)
+    return I.perturbation_variables(q, phi, rbar, pbar), np.stack([rbar, pbar])
+
+
+@pytest.mark.parametrize("N", range(1, 9))
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_steps_every_order(N, dtype):
+    """Two steps on a warped closed mesh with a strongly varying smooth state,
+    with the Coriolis source, in full and in perturbation variables."""
+    K = (3, 2, 2)
+    periodic = (True, N % 2 == 0, N % 3 != 0)
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, periodic, seed=500 + N)
+    X = I.box_mesh(K, (0, 0, 0), tuple(1000.0 * k for k in K), N, warp_frac=0.05, seed=500 + N)
+    X = X.reshape(3, X.shape[1], -1)
+    omega = (1.0e-4, -2.0e-4, 1.4e-4)
+    dt = 0.01
+    qd, phid, geomd, Dd = (a.astype(dtype) for a in (q, phi, geom, D))
+    got = gpu_steps(qd, phid, geomd, Dd, nbr, dt, 2, omega=omega)
+    stepped_check(got, qd, phid, geomd, Dd, nbr, N, dt, 2, dtype, omega=omega,
+                  label=f"N={N} {np.dtype(dtype).name}")
+    qp, ref = perturbed(q, phi, X)
+    qp, ref = qp.astype(dtype), ref.astype(dtype)
+    got = gpu_steps(qp, phid, geomd, Dd, nbr, dt, 2, ref=ref, omega=omega)
+    stepped_check(got, qp, phid, geomd, Dd, nbr, N, dt, 2, dtype, ref=ref, omega=omega,
+                  label=f"N={N} {np.dtype(dtype).name} perturbation variables")
+
+
+@pytest.mark.parametrize("name,dtype", [("tiny", np.float64), ("tiny", np.float32),
+                                        ("bubble", np.float64), ("bubble_f32", np.float32)])
+def test_steps_workloads(name, dtype):
+    """Three steps of the tiny and bubble workloads at a time step near their
+    acoustic limit (0.5 min node spacing / sound speed)."""
+    wl = I.make(name)
+    dt = {"tiny": 1.0e-4, "bubble": 7.0e-3, "bubble_f32": 7.0e-3}[name]
+    got = gpu_steps(wl.q, wl.phi, wl.geom, wl.D, wl.nbr, dt, 3)
+    stepped_check(got, wl.q, wl.phi, wl.geom, wl.D, wl.nbr, wl.N, dt, 3, dtype, label=name)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_stage_entry_point(dtype):
+    """Five calls of the stage entry point with the oracle's published
+    coefficients are one step of the oracle's scheme; the stages ping-pong
+    between two state buffers."""
+    N = 3
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, (3, 2, 1), (True, True, False), seed=77)
+    q, phi, geom, D = (a.astype(dtype) for a in (q, phi, geom, D))
+    A, B = oracle.default().lsrk_coefficients()
+    dt = 0.01
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    tn = torch.from_numpy(nbr).to(dev())
+    dq = torch.full_like(tq, float("nan"))   # the first stage must not read it
+    other = torch.empty_like(tq)
+    src, dst = tq, other
+    for s in range(5):
+        esdg.lsrk_stage(src, tp, tg, tD, tn, A[s], B[s], dt, dq, q_out=dst)
+        src, dst = dst, src
+    torch.cuda.synchronize()
+    stepped_check(src.cpu().numpy(), q, phi, geom, D, nbr, N, dt, 1, dtype,
+                  label=f"five stage calls {np.dtype(dtype).name}")
+
+
+def test_steps_ragged_meshes():
+    """Element counts that leave the last workgroup partly empty, an odd and an
+    even step count (the final copy back into q, or none)."""
+    for K in ((7, 1, 1), (5, 1, 2)):
+        for nsteps in (1, 2):
+            q, phi, geom, D, nbr, _ = random_closed_mesh(4, K, (True, True, True), seed=sum(K))
+            got = gpu_steps(q, phi, geom, D, nbr, 0.01, nsteps)
+            stepped_check(got, q, phi, geom, D, nbr, 4, 0.01, nsteps, np.float64,
+                          label=f"K={K} steps={nsteps}")
+
+
+def test_zero_steps_and_empty_mesh():
+    wl = I.make("tiny")
+    got = gpu_steps(wl.q, wl.phi, wl.geom, wl.D, wl.nbr, 0.1, 0)
+    assert np.array_equal(got, wl.q)
+    Np = 64
+    z = lambda *s: torch.zeros(*s, dtype=torch.float64, device=dev())
+    q = z(5, 0, Np)
+    esdg.lsrk_steps(q, z(0, Np), z(10, 0, Np), z(4, 4),
+                    torch.zeros(0, 6, dtype=torch.int32, device=dev()), 0.1, 3)
+    torch.cuda.synchronize()
+
+
+def test_steps_graph_capture_and_replay():
+    """The steps allocate nothing and issue no memset: captured once in a HIP
+    graph (through torch's graph API, an odd stage count so the final copy
+    is in the graph too) and replayed with eager work between replays, every
+    replay reproduces an eager call bitwise."""
+    wl = I.make("tiny")
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    tn = torch.from_numpy(wl.nbr).to(dev())
+    q_tmp, dq = torch.empty_like(tq), torch.empty_like(tq)
+    base = tq.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        esdg.lsrk_steps(tq, tp, tg, tD, tn, 1e-4, 1, q_tmp=q_tmp, dq=dq)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        esdg.lsrk_steps(tq, tp, tg, tD, tn, 1e-4, 1, q_tmp=q_tmp, dq=dq)
+    for rep in range(4):
+        start = base.clone()
+        start[4].mul_(1.0 + 1e-4 * rep)
+        ref = start.clone()
+        esdg.lsrk_steps(ref, tp, tg, tD, tn, 1e-4, 1)
+        torch.cuda.synchronize()
+        tq.copy_(start)
+        q_tmp.fill_(float("nan"))
+        dq.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tq, ref), rep
+
+
+# --- perturbation variables: the right-hand side ---------------------------------------
+def gpu_rhs_pert(qp, ref, phi, geom, D, nbr, omega=None):
+    tq, tr, tp, tg, tD = to_gpu(qp, ref, phi, geom, D)
+    tn = torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev())
+    out = esdg.rhs_pert(tq, tr, tp, tg, tD, tn, omega=omega)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def gpu_rhs(q, phi, geom, D, nbr):
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    tn = torch.from_numpy(np.ascontiguousarray(nbr, dtype=np.int32)).to(dev())
+    out = esdg.rhs(tq, tp, tg, tD, tn)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def rhs_errors(got, ref, mag):
+    got = got.astype(np.float64)
+    by_mag = [float(np.abs(got[f] - ref[f]).max() / np.abs(mag[f]).max()) for f in range(5)]
+    by_rhs = [float(np.abs(got[f] - ref[f]).max() / max(np.abs(ref[f]).max(), 1e-300))
+              for f in range(5)]
+    return by_mag, by_rhs
+
+
+@pytest.mark.parametrize("name", ["tiny", "bubble", "baroclinic", "bubble_f32"])
+def test_rhs_pert_workloads(name):
+    wl, qp, ref = I.make_perturbed(name)
+    dtype = qp.dtype.type
+    got = gpu_rhs_pert(qp, ref, wl.phi, wl.geom, wl.D, wl.nbr)
+    full = oracle.full_state(qp, ref, wl.phi)
+    want, mag = oracle.rhs(full, wl.phi, wl.geom, wl.D, wl.nbr, wl.N, with_magnitude=True)
+    by_mag, by_rhs = rhs_errors(got, want, mag)
+    print(f"[pert] {name}: err/max mag {['%.1e' % e for e in by_mag]}  "
+          f"err/max|rhs| {['%.1e' % e for e in by_rhs]}", flush=True)
+    assert max(by_mag) <= TOL[dtype], (name, by_mag)
+
+
+@pytest.mark.parametrize("N", range(1, 9))
+def test_rhs_pert_every_order(N):
+    K = (3, 2, 2)
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, (True, False, True), seed=900 + N)
+    X = I.box_mesh(K, (0, 0, 0), tuple(1000.0 * k for k in K), N, warp_frac=0.05, seed=900 + N)
+    qp, ref = perturbed(q, phi, X.reshape(3, X.shape[1], -1))
+    for dtype in (np.float64, np.float32):
+        a = [x.astype(dtype) for x in (qp, ref, phi, geom, D)]
+        got = gpu_rhs_pert(*a, nbr, omega=(0.0, 1e-4, 2e-4))
+        full = oracle.full_state(a[0], a[1], a[2])
+        want, mag = oracle.rhs(full, a[2], a[3], a[4], nbr, N, omega=np.array([0.0, 1e-4, 2e-4]),
+                               with_magnitude=True)
+        by_mag, _ = rhs_errors(got, want, mag)
+        print(f"[pert] N={N} {np.dtype(dtype).name}: err/max mag {['%.1e' % e for e in by_mag]}",
+              flush=True)
+        assert max(by_mag) <= TOL[dtype], (N, dtype, by_mag)
+
+
+def test_fp32_noise_full_against_perturbation_variables():
+    """The measurement the page's remark calls for ([ESDG-GPU §5.2]): the fp32
+    whole right-hand side of the near-balanced bubble against the oracle on
+    the same represented state, error over max |rhs| itself, with full state
+    variables and with perturbation variables about the hydrostatic base.
+    Both must meet the parity bar (over the summed magnitudes); the printed
+    figures are what the comparison shows."""
+    wl32 = I.make("bubble_f32")
+    got_full = gpu_rhs(wl32.q, wl32.phi, wl32.geom, wl32.D, wl32.nbr)
+    want_full, mag_full = oracle.rhs(wl32.q, wl32.phi, wl32.geom, wl32.D, wl32.nbr, wl32.N,
+                                     with_magnitude=True)
+    _, qp, ref = I.make_perturbed("bubble_f32")
+    got_pert = gpu_rhs_pert(qp, ref, wl32.phi, wl32.geom, wl32.D, wl32.nbr)
+    full = oracle.full_state(qp, ref, wl32.phi)
+    want_pert, mag_pert = oracle.rhs(full, wl32.phi, wl32.geom, wl32.D, wl32.nbr, wl32.N,
+                                     with_magnitude=True)
+    m_full, r_full = rhs_errors(got_full, want_full, mag_full)
+    m_pert, r_pert = rhs_errors(got_pert, want_pert, mag_pert)
+    print(f"[pert] bubble fp32 full state:    err/max|rhs| {['%.2e' % e for e in r_full]}", flush=True)
+    print(f"[pert] bubble fp32 perturbations: err/max|rhs| {['%.2e' % e for e in r_pert]}", flush=True)
+    assert max(m_full) <= TOL[np.float32] and max(m_pert) <= TOL[np.float32]
+
+
+# --- conservation integrals ------------------------------------------------------------
+def gpu_integrals(q, phi, geom, w, ref=None):
+    tq, tp, tg, tw = to_gpu(q, phi, geom, w)
+    tr = to_gpu(ref)[0] if ref is not None else None
+    out = esdg.integrals(tq, tp, tg, tw, ref=tr)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "bubble", "baroclinic", "bubble_f32", "high_order"])
+def test_integrals_workloads(name):
+    wl = I.make(name)
+    _, w = I.lgl(wl.N)
+    w = w.astype(wl.q.dtype)
+    got = gpu_integrals(wl.q, wl.phi, wl.geom, w)
+    want = oracle.integrals(wl.q, wl.phi, wl.geom, w, wl.N)
+    rel = np.abs(got - want) / np.abs(want)
+    print(f"[integrals] {name}: {got} rel. diff {rel}", flush=True)
+    assert np.all(rel <= 1e-12), rel
+    wl_, qp, ref = I.make_perturbed(name)
+    got = gpu_integrals(qp, wl.phi, wl.geom, w, ref=ref)
+    want = oracle.integrals(oracle.full_state(qp, ref, wl.phi), wl.phi, wl.geom, w, wl.N)
+    rel = np.abs(got - want) / np.abs(want)
+    print(f"[integrals] {name} perturbation variables: rel. diff {rel}", flush=True)
+    assert np.all(rel <= 1e-12), rel
+
+
+def test_integrals_small_and_empty():
+    for ne in (1, 3):
+        wl = I.make("tiny")
+        q, phi, geom = wl.q[:, :ne], wl.phi[:ne], wl.geom[:, :ne]
+        _, w = I.lgl(wl.N)
+        got = gpu_integrals(q, phi, geom, w)
+        want = oracle.integrals(q, phi, geom, w, wl.N)
+        assert np.all(np.abs(got - want) <= 1e-13 * np.abs(want)), (ne, got, want)
+    z = lambda *s: torch.zeros(*s, dtype=torch.float64, device=dev())
+    out = esdg.integrals(z(5, 0, 8), z(0, 8), z(10, 0, 8), z(2))
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [0.0, 0.0, 0.0]
+
+
+def test_conservation_over_steps_on_gpu():
+    """The GPU's own stepped states keep the integrals of rho and E on a
+    closed mesh to round-off (fp64), measured by the GPU integrals."""
+    N, K = 4, (3, 2, 2)
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, (True, True, False), seed=31)
+    _, w = I.lgl(N)
+    i0 = gpu_integrals(q, phi, geom, w)
+    got = gpu_steps(q, phi, geom, D, nbr, 0.01, 5)
+    i1 = gpu_integrals(got, phi, geom, w)
+    rel = (i1 - i0) / np.abs(i0)
+    print(f"[time] drift over 5 steps (mass, energy, entropy): {rel}", flush=True)
+    assert abs(rel[0]) <= 1e-14 and abs(rel[1]) <= 1e-14, rel
