@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "esdg.h"
 #include "volume_kernel.hpp"
 #include "integrals_kernel.hpp"
@@ -291,6 +293,43 @@ int integrals(const T *q, const T *ref, const T *phi, const T *geom, const T *w,
     return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
 }
 
+// The allocation-free variant of the integrals keeps its partial sums in
+// this file-scope device array (one copy per device, held until the process
+// ends) instead of a caller's workspace.  Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and is kept below.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+double *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) double scratch[3 * kIntegralBlocks];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device); NULL with *status set when the device cannot be queried.
+double *scratch_on_current_device(int *status)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *status = ESDG_ERR_DEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            *status = ESDG_ERR_DEVICE;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<double *>(p);
+    }
+    *status = ESDG_OK;
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 }  // namespace esdg
 
@@ -409,6 +448,20 @@ int esdg_integrals_f32(const float *q, const float *ref, const float *phi, const
     return esdg::integrals<float>(q, ref, phi, geom, w, N, nelem, work, out, stream);
 }
 
+int esdg_integrals_noalloc_f64(const double *q, const double *ref, const double *phi,
+                               const double *geom, const double *w, int N, int64_t nelem,
+                               double *out, hipStream_t stream)
+{
+    esdg::Sizes z;
+    if (int st = esdg::check_sizes<double>(N, nelem, z)) return st;
+    // the partial sums never exceed the array: at most kIntegralBlocks per call
+    if (esdg::integral_blocks(nelem * z.Np) > esdg::kIntegralBlocks) return ESDG_ERR_NELEM;
+    int st = ESDG_OK;
+    double *part = esdg::scratch_on_current_device(&st);
+    if (!part) return st;
+    return esdg::integrals<double>(q, ref, phi, geom, w, N, nelem, part, out, stream);
+}
+
 const char *esdg_status_string(int status)
 {
     switch (status) {
@@ -418,6 +471,7 @@ const char *esdg_status_string(int status)
         case ESDG_ERR_NELEM: return "nelem is negative or too large";
         case ESDG_ERR_LAUNCH: return "kernel launch failed";
         case ESDG_ERR_ALIAS: return "an output overlaps an input or another output";
+        case ESDG_ERR_DEVICE: return "the current device or its scratch array could not be located";
     }
     return "unknown status";
 }

@@ -22,13 +22,15 @@ ESDG_ERR_ORDER = -2
 ESDG_ERR_NELEM = -3
 ESDG_ERR_LAUNCH = -4
 ESDG_ERR_ALIAS = -5
+ESDG_ERR_DEVICE = -6
 
 # every symbol include/esdg.h declares
 EXPORTS = ("esdg_volume_rhs_f64", "esdg_volume_rhs_f32", "esdg_rhs_f64", "esdg_rhs_f32",
            "esdg_rhs_pert_f64", "esdg_rhs_pert_f32", "esdg_lsrk_stage_f64", "esdg_lsrk_stage_f32",
            "esdg_lsrk_steps_f64", "esdg_lsrk_steps_f32", "esdg_lsrk_stages",
            "esdg_lsrk_coefficients", "esdg_integrals_workspace_bytes", "esdg_integrals_f64",
-           "esdg_integrals_f32", "esdg_status_string", "esdg_min_order", "esdg_max_order")
+           "esdg_integrals_f32", "esdg_integrals_noalloc_f64", "esdg_status_string",
+           "esdg_min_order", "esdg_max_order")
 
 
 class EsdgError(RuntimeError):
@@ -84,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ci
         fn.argtypes = [vp, vp, vp, vp, vp, ci, i64, vp, vp, vp]
+    lib.esdg_integrals_noalloc_f64.restype = ci
+    lib.esdg_integrals_noalloc_f64.argtypes = [vp, vp, vp, vp, vp, ci, i64, vp, vp]
     lib.esdg_status_string.restype = ctypes.c_char_p
     lib.esdg_status_string.argtypes = [ci]
     lib.esdg_min_order.restype = ci
@@ -199,6 +203,11 @@ def esdg_integrals_f64(q: int, ref: int, phi: int, geom: int, w: int, N: int, ne
 def esdg_integrals_f32(q: int, ref: int, phi: int, geom: int, w: int, N: int, nelem: int,
                        work: int, out: int, stream: int = 0) -> int:
     return load().esdg_integrals_f32(q, ref, phi, geom, w, N, nelem, work, out, stream)
+
+
+def esdg_integrals_noalloc_f64(q: int, ref: int, phi: int, geom: int, w: int, N: int,
+                               nelem: int, out: int, stream: int = 0) -> int:
+    return load().esdg_integrals_noalloc_f64(q, ref, phi, geom, w, N, nelem, out, stream)
 
 
 def esdg_status_string(status: int) -> str:
@@ -376,6 +385,29 @@ def integrals(q, phi, geom, w, ref=None, work=None, out=None, stream=None):
         _check(fn(q.data_ptr(), ref.data_ptr() if ref is not None else None, phi.data_ptr(),
                   geom.data_ptr(), w.data_ptr(), N, nelem, work.data_ptr(), out.data_ptr(),
                   _stream_handle(stream, q.device)))
+    return out
+
+
+def integrals_noalloc(q, phi, geom, w, out, ref=None, stream=None):
+    """integrals() of a float64 state through the allocation-free entry point:
+    `out` (device float64 [3]) is the caller's; the partial sums use the
+    library's own device array."""
+    import torch
+
+    Nq = w.shape[0]
+    D_dummy = torch.empty((Nq, Nq), dtype=q.dtype, device=q.device)
+    N, nelem = _validate(q, phi, geom, D_dummy, None, ref)
+    if q.dtype != torch.float64:
+        raise TypeError("the allocation-free integrals take float64 states")
+    if w.dtype != q.dtype or w.device != q.device or not w.is_contiguous() or w.dim() != 1:
+        raise ValueError("w must be a contiguous 1-D tensor like q")
+    if (out.dtype != torch.float64 or out.device != q.device or out.numel() != 3
+            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous float64 tensor of 3 values on q's device")
+    with torch.cuda.device(q.device):
+        _check(esdg_integrals_noalloc_f64(q.data_ptr(), ref.data_ptr() if ref is not None else None,
+                                          phi.data_ptr(), geom.data_ptr(), w.data_ptr(), N, nelem,
+                                          out.data_ptr(), _stream_handle(stream, q.device)))
     return out
 
 

@@ -60,6 +60,8 @@ extern "C" {
 #define ESDG_ERR_NELEM  (-3)  /* nelem < 0, or the arrays would not be addressable  */
 #define ESDG_ERR_LAUNCH (-4)  /* the kernel launch failed (hipGetLastError)         */
 #define ESDG_ERR_ALIAS  (-5)  /* an output overlaps an input or another output      */
+#define ESDG_ERR_DEVICE (-6)  /* the current device (or its scratch array) could not
+                                 be located: esdg_integrals_noalloc_f64 only          */
 
 /* Volume term in fp64 arithmetic. Returns a status code above. */
 int esdg_volume_rhs_f64(const double *q, const double *phi, const double *geom,
@@ -219,6 +221,26 @@ int esdg_integrals_f64(const double *q, const double *ref, const double *phi, co
 int esdg_integrals_f32(const float *q, const float *ref, const float *phi, const float *geom,
                        const float *w, int N, int64_t nelem, double *work, double *out,
                        hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * integrals as esdg_integrals_f64, without the `work` argument.  The partial
+ * sums go to a file-scope device array of the library instead, 3 * 1024
+ * doubles (24 KiB) on every device the library runs on, held until the
+ * process ends; its address on the current device is looked up on the first
+ * call on that device (ESDG_ERR_DEVICE if that fails).  The call allocates
+ * nothing.  Any nelem fits: a call writes at most 1024 partial sums (the
+ * nodes are split over at most 1024 workgroups); a size needing more would
+ * be rejected with ESDG_ERR_NELEM.  Every partial sum a call reads is written
+ * earlier in the same call, so nothing needs clearing between calls.
+ * Calls on one device share its array: calls that overlap in time on one
+ * device (other streams, other host threads) race and give wrong sums; order
+ * them on one stream.  Everything else as esdg_integrals_f64.
+ */
+int esdg_integrals_noalloc_f64(const double *q, const double *ref, const double *phi,
+                               const double *geom, const double *w, int N, int64_t nelem,
+                               double *out, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *esdg_status_string(int status);

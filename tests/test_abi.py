@@ -65,7 +65,7 @@ def test_order_range_and_status_strings():
     assert esdg.esdg_min_order() == 1
     assert esdg.esdg_max_order() == 8
     for st in (esdg.ESDG_OK, esdg.ESDG_ERR_NULL, esdg.ESDG_ERR_ORDER, esdg.ESDG_ERR_NELEM,
-               esdg.ESDG_ERR_LAUNCH, esdg.ESDG_ERR_ALIAS):
+               esdg.ESDG_ERR_LAUNCH, esdg.ESDG_ERR_ALIAS, esdg.ESDG_ERR_DEVICE):
         s = esdg.esdg_status_string(st)
         assert s and s != "unknown status"
     assert esdg.esdg_status_string(12345) == "unknown status"
