@@ -5,14 +5,17 @@ the geopotential and 10 geometry values (9 metric terms and J) and write 5
 fields: 21 values = 168 B in fp64, 84 B in fp32.  The differentiation matrix
 (N+1)^2 values per launch is added once.
 
-FLOP counting convention (counted from the kernel's arithmetic; the method's
-work, not the ordered-pair work the symmetric evaluation avoids):
-  +, -, x, / and reciprocal = 1 FLOP, fused multiply-add = 2, log = 1;
-  comparisons and selects = 0; the log means are counted on their series
-  branch; quantities hoisted per node are counted once per node.
-  per unordered pair on a line ........ 120
-  per node (primitives, p, b, 2 logs,
-            1/b, direction sum, -1/J) ...  38
+FLOP counting convention (the method's work, not the ordered-pair work the
+symmetric evaluation avoids): +, -, x, reciprocal and log = 1 FLOP, fused
+multiply-add = 2; comparisons, selects and negations = 0; the log means are
+counted on their series branch (the branch smooth flows take); quantities
+hoisted per node are counted once per node.  The tallies below follow the
+kernel's pair and node arithmetic step by step (pair_update and node_values
+of csrc/volume_kernel.hpp, series form):
+
+  per unordered pair on a line ........ 96   (PAIR_STEPS)
+  per node ............................ 45   (NODE_STEPS)
+
 Unordered pairs per element: 3 (N+1)^2 (N+1) N / 2.
 
 Whole right-hand side (volume + entropy-conservative surface term, one fused
@@ -20,13 +23,57 @@ kernel): the algorithmic traffic adds only the connectivity, 6 int32 per
 element; the kernel also re-reads each face partner's 5 fields and phi from
 the neighbouring element (48 B per face node in fp64 with a neighbour, none at
 a slip wall), which the cache may or may not serve.  Work per face node: one
-pair (120) plus the partner's per-node values (38) with a neighbour; one pair
-and the mirror state (12) at a slip wall.
+pair plus the partner's per-node values (its primitives, p, b, 2 logs, 1/b,
+w: NODE_STEPS without the -1/J and the directional sum) with a neighbour; one
+pair and the mirror state at a slip wall.
 """
 from __future__ import annotations
 
-FLOP_PER_PAIR = 120
-FLOP_PER_NODE = 38
+# (step, {operation: count}) with operation in add (also sub), mul, fma, rcp, log
+PAIR_STEPS = (
+    ("sums and jumps of rho and b", {"add": 4}),
+    ("one reciprocal for 1/(rho_a+rho_l) and 1/(b_a+b_l)", {"mul": 1, "rcp": 1}),
+    ("1/(rho_a+rho_l), 1/(b_a+b_l)", {"mul": 2}),
+    ("log mean of rho: s, s^2, cubic series in s^2, scale", {"mul": 3, "fma": 3}),
+    ("inverse log mean of b: s, s^2, cubic series in s^2, scale", {"mul": 3, "fma": 3}),
+    ("{{rho}}/(2{{b}})", {"mul": 2}),
+    ("pair metric Ja^k(a) + Ja^k(l)", {"add": 3}),
+    ("2{{u}}", {"add": 3}),
+    ("contravariant density flux", {"mul": 2, "fma": 2}),
+    ("symmetric momentum flux", {"mul": 3, "fma": 3}),
+    ("energy-flux coefficient", {"add": 1, "fma": 1}),
+    ("energy flux", {"mul": 1, "fma": 3}),
+    ("gravity term g", {"add": 1, "mul": 2}),
+    ("gravity for each node: g/b_a, -g/b_l", {"mul": 2}),
+    ("density and energy contributions to both nodes", {"fma": 4}),
+    ("momentum contributions with gravity to both nodes", {"fma": 12}),
+)
+NODE_STEPS = (
+    ("1/rho, 1/(2 rho)", {"rcp": 1, "mul": 1}),
+    ("u/2", {"mul": 3}),
+    ("|u|^2/4", {"mul": 1, "fma": 2}),
+    ("E - U.u/2... - rho phi", {"mul": 1, "fma": 3, "add": 1}),
+    ("p", {"mul": 1}),
+    ("scaled b = s_b rho/(2p)", {"rcp": 1, "mul": 2}),
+    ("1/b", {"mul": 2}),
+    ("ln rho, ln b", {"log": 2}),
+    ("phi/4", {"mul": 1}),
+    ("w/2 = (phi - |u|^2/2)/2", {"fma": 1}),
+    ("-1/J", {"rcp": 1}),
+    ("sum of the three directional partials", {"add": 10}),
+    ("scale by -1/J", {"mul": 5}),
+)
+WEIGHT = {"add": 1, "mul": 1, "fma": 2, "rcp": 1, "log": 1}
+
+
+def tally(steps) -> int:
+    return sum(WEIGHT[op] * n for _, ops in steps for op, n in ops.items())
+
+
+FLOP_PER_PAIR = tally(PAIR_STEPS)
+FLOP_PER_NODE = tally(NODE_STEPS)
+# a face partner's node values: NODE_STEPS without -1/J, the directional sum and the scaling
+FLOP_PER_PARTNER_NODE = FLOP_PER_NODE - tally(NODE_STEPS[-3:])
 
 # MI355X (gfx950) published peaks
 PEAK_HBM_GBS = 8000.0          # HBM3E, GB/s
@@ -77,7 +124,7 @@ def surface_flops(N: int, nbr) -> int:
     walls = int((nbr < 0).sum())
     faces = int(nbr.size)
     per_face = (N + 1) ** 2
-    return ((faces - walls) * per_face * (FLOP_PER_PAIR + FLOP_PER_NODE)
+    return ((faces - walls) * per_face * (FLOP_PER_PAIR + FLOP_PER_PARTNER_NODE)
             + walls * per_face * (FLOP_PER_PAIR + FLOP_PER_MIRROR))
 
 

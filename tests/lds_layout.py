@@ -21,7 +21,7 @@ import re
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-API_SOURCE = os.path.join(HERE, "csrc", "esdg_api.hip")
+API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "esdg_api.hip")
 
 # LaunchCfg<EPB, NT, WAVES, METRIC_LDS, CACHE, KMAJOR, FIN, SERIES, SERIES_SURF,
 #           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF> and its defaults

@@ -6,7 +6,7 @@ numbering, and the padded shapes cost no more LDS bank cycles than the
 unpadded grid in the bank model that chose them."""
 import pytest
 
-from entropy_stable_dg_amd import lds_layout as L
+from tests import lds_layout as L
 
 TABLE = L.parse_launch_table()
 CASES = sorted(TABLE)

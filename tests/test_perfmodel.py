@@ -1,0 +1,33 @@
+"""The analytic work model: the per-pair and per-node FLOP tallies are the
+sums of their itemised steps under the stated weights, and the figures the
+benchmark reports follow from them."""
+from entropy_stable_dg_amd import perfmodel as P
+
+
+def test_weights_of_the_convention():
+    assert P.WEIGHT == {"add": 1, "mul": 1, "fma": 2, "rcp": 1, "log": 1}
+
+
+def test_pair_tally():
+    by_op = {}
+    for _, ops in P.PAIR_STEPS:
+        for op, n in ops.items():
+            by_op[op] = by_op.get(op, 0) + n
+    # series form of the pair: 12 adds, 21 multiplies, 31 fused multiply-adds, 1 reciprocal
+    assert by_op == {"add": 12, "mul": 21, "fma": 31, "rcp": 1}
+    assert P.FLOP_PER_PAIR == 12 + 21 + 2 * 31 + 1 == 96
+
+
+def test_node_tally():
+    assert P.FLOP_PER_NODE == 45
+    assert P.FLOP_PER_PARTNER_NODE == 45 - 1 - 10 - 5
+
+
+def test_per_dof_figures():
+    # pairs per element 3 Nq^2 Nq N/2; per DOF 3N/2
+    for N in range(1, 9):
+        assert P.pairs_per_element(N) == 3 * (N + 1) ** 3 * N // 2
+        assert abs(P.flops_per_dof(N) - (1.5 * N * 96 + 45)) < 1e-12
+    assert P.flops_per_dof(4) == 621.0
+    assert abs(P.arithmetic_intensity(4, "f64") - 621.0 / 168.0) < 1e-12
+    assert P.bytes_per_dof("f64") == 168 and P.bytes_per_dof("f32") == 84
