@@ -107,13 +107,15 @@ def preroll(run, sync, seconds: float = PREROLL_S) -> int:
 
 
 def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full: bool = False,
-                  graph: bool = False):
+                  graph: bool = False, two_lane: bool = False):
     """Returns (seconds per step rotating cold buffers, seconds per step hot, info).
     With `full`, the whole right-hand side (volume + surface, esdg_rhs_*).
     With `graph`, the steps are captured once in a HIP graph (through torch's
     graph API) and the graph is replayed: the same launches without the
     per-launch host overhead.  Before each timed pass: `warmup` launches and
-    a pre-roll of at least PREROLL_S seconds (preroll())."""
+    a pre-roll of at least PREROLL_S seconds (preroll()).  With `two_lane`,
+    the volume term by the two-lanes-per-line variant of the production kernel
+    (libesdg_ablation, fp64, N = 5 and 7), for comparison."""
     import torch
 
     from entropy_stable_dg_amd import esdg, inputs, perfmodel
@@ -133,9 +135,14 @@ def time_workload(name: str, steps: int, warmup: int, rotate_bytes: float, full:
         sets.append((q, phi, geom, D, nbr, rhs))
     if full:
         fn = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
+    elif two_lane:
+        from entropy_stable_dg_amd import ablation
+
+        if dtype != "f64" or wl.N not in ablation.TWO_LANE_ORDERS:
+            raise ValueError("the two-lane variant is fp64 at N = 5, 7")
+        fn = ablation.esdg_ablation_two_lane_volume_rhs_f64
     else:
         fn = esdg.esdg_volume_rhs_f64 if dtype == "f64" else esdg.esdg_volume_rhs_f32
-        fn_rhs = esdg.esdg_rhs_f64 if dtype == "f64" else esdg.esdg_rhs_f32
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
     ptrs = [(q.data_ptr(), phi.data_ptr(), geom.data_ptr(), D.data_ptr(), nbr.data_ptr(),
@@ -328,7 +335,8 @@ def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
     torch.cuda.synchronize()
     del src, dst
     name, _, mode = workload.partition(":")
-    cold, hot, info, _ = time_workload(name, steps, 2, 512e6, full=(mode == "rhs"))
+    cold, hot, info, _ = time_workload(name, steps, 2, 512e6, full=(mode == "rhs"),
+                                       two_lane=(mode == "two_lane"))
     return {"profile_pass": True, "workload": workload, "copy_bytes_each_way": n * 8,
             "us_per_step": cold * 1e6, "bytes_per_launch": info["bytes"],
             "flops_per_launch": info["flops"], "kernel_source_hash": kernel_source_hash()}
@@ -598,8 +606,10 @@ def main() -> int:
                     help="short run for rocprofv3 counter passes (copy calibration + kernel)")
     ap.add_argument("--workload", default=HEADLINE,
                     help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, "
-                         "high_order; a ':rhs' suffix profiles the whole right-hand side)")
-    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,high_order",
+                         "high_order; a ':rhs' suffix profiles the whole right-hand side, "
+                         "':two_lane' the two-lanes-per-line variant)")
+    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,high_order,"
+                                       "high_order:two_lane",
                     help="comma-separated extra workloads to time (reported under 'extra'); "
                          "a ':rhs' suffix times the whole right-hand side (volume + surface), "
                          "':graph' replays the launches from a captured HIP graph")
@@ -660,7 +670,7 @@ def main() -> int:
         name, _, mode = key.partition(":")
         full = mode == "rhs"
         c, h, inf, _ = time_workload(name, args.steps, args.warmup, args.rotate_mb * 1e6, full=full,
-                                     graph=(mode == "graph"))
+                                     graph=(mode == "graph"), two_lane=(mode == "two_lane"))
         extra[key] = {
             "dof_per_s": inf["dof"] / c, "us_per_step": c * 1e6, "hot_us_per_step": h * 1e6,
             "hbm_gbs_algorithmic": inf["bytes"] / c / 1e9, "gflops_analytic": inf["flops"] / c / 1e9,
@@ -681,6 +691,9 @@ def main() -> int:
                 fl32 / c / 1e12 / perfmodel.PEAK_FP32_VECTOR_TFLOPS if fl32 else None)
         if mode == "graph":
             extra[key]["what"] = "the same launches captured once in a HIP graph and replayed"
+        if mode == "two_lane":
+            extra[key]["what"] = ("the production kernel with two lanes per grid line and a "
+                                  "cross-lane exchange (libesdg_ablation), for comparison")
         if full:
             extra[key]["hbm_gbs_with_face_partners"] = inf["bytes_with_face_partners"] / c / 1e9
             extra[key]["what"] = "whole right-hand side: volume + entropy-conservative surface term"

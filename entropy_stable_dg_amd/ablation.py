@@ -10,7 +10,9 @@ from .esdg import ESDG_OK, EsdgError, esdg_status_string
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ABLATION_LIB_PATH = os.path.join(HERE, "libesdg_ablation.so")
-EXPORTS = ("esdg_ablation_volume_rhs_f64", "esdg_ablation_name")
+EXPORTS = ("esdg_ablation_volume_rhs_f64", "esdg_ablation_two_lane_volume_rhs_f64",
+           "esdg_ablation_name")
+TWO_LANE_ORDERS = (5, 7)
 
 ESDG_ABL_BASELINE = 0
 ESDG_ABL_HOIST = 1
@@ -42,6 +44,8 @@ def load(path: str = ABLATION_LIB_PATH) -> ctypes.CDLL:
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.esdg_ablation_volume_rhs_f64.restype = ci
     lib.esdg_ablation_volume_rhs_f64.argtypes = [ci, vp, vp, vp, vp, ci, i64, vp, vp]
+    lib.esdg_ablation_two_lane_volume_rhs_f64.restype = ci
+    lib.esdg_ablation_two_lane_volume_rhs_f64.argtypes = [vp, vp, vp, vp, ci, i64, vp, vp]
     lib.esdg_ablation_name.restype = ctypes.c_char_p
     lib.esdg_ablation_name.argtypes = [ci]
     if path == ABLATION_LIB_PATH:
@@ -52,6 +56,11 @@ def load(path: str = ABLATION_LIB_PATH) -> ctypes.CDLL:
 def esdg_ablation_volume_rhs_f64(variant: int, q: int, phi: int, geom: int, D: int, N: int,
                                  nelem: int, rhs: int, stream: int = 0) -> int:
     return load().esdg_ablation_volume_rhs_f64(variant, q, phi, geom, D, N, nelem, rhs, stream)
+
+
+def esdg_ablation_two_lane_volume_rhs_f64(q: int, phi: int, geom: int, D: int, N: int, nelem: int,
+                                          rhs: int, stream: int = 0) -> int:
+    return load().esdg_ablation_two_lane_volume_rhs_f64(q, phi, geom, D, N, nelem, rhs, stream)
 
 
 def esdg_ablation_name(variant: int) -> str:
@@ -85,4 +94,27 @@ def volume_rhs(variant, q, phi, geom, D, out=None, stream=None):
     if st != ESDG_OK:
         msg = "unknown ablation variant" if st == ESDG_ERR_VARIANT else esdg_status_string(st)
         raise EsdgError(st, msg)
+    return out
+
+
+def two_lane_volume_rhs(q, phi, geom, D, out=None, stream=None):
+    """The production volume kernel with two lanes per grid line (N = 5, 7),
+    on float64 GPU tensors shaped as for esdg.volume_rhs."""
+    import torch
+
+    N = D.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    for name, t in (("q", q), ("phi", phi), ("geom", geom), ("D", D), ("out", out)):
+        if t.dtype != torch.float64 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float64 GPU tensor")
+    with torch.cuda.device(q.device):
+        st = esdg_ablation_two_lane_volume_rhs_f64(q.data_ptr(), phi.data_ptr(), geom.data_ptr(),
+                                                   D.data_ptr(), N, q.shape[1], out.data_ptr(),
+                                                   handle)
+    if st != ESDG_OK:
+        raise EsdgError(st, esdg_status_string(st))
     return out

@@ -427,6 +427,40 @@ int esdg_ablation_volume_rhs_f64(int variant, const double *q, const double *phi
     return ESDG_ERR_ORDER;
 }
 
+int esdg_ablation_two_lane_volume_rhs_f64(const double *q, const double *phi, const double *geom,
+                                          const double *D, int N, int64_t nelem, double *rhs,
+                                          hipStream_t stream)
+{
+    // LaunchCfg<EPB, NT, waves, metric in LDS, line cache, direction-major, FIN, series,
+    // series (surface), row pad, plane pad, element pad, waves (surface), lanes per line>
+    using C5 = esdg::LaunchCfg<1, 256, 3, false, false, 1, false, true, false, 0, 0, 0, 0, 2>;
+    using C7 = esdg::LaunchCfg<1, 384, 3, false, false, 1, true, true, false, 1, 0, 0, 0, 2>;
+    if (N != 5 && N != 7) return ESDG_ERR_ORDER;
+    if (nelem < 0) return ESDG_ERR_NELEM;
+    if (nelem == 0) return ESDG_OK;
+    if (!q || !phi || !geom || !D || !rhs) return ESDG_ERR_NULL;
+    if (nelem > INT32_MAX) return ESDG_ERR_NELEM;  // one workgroup per element
+    const int64_t Np = (int64_t)(N + 1) * (N + 1) * (N + 1);
+    const uintptr_t r0 = (uintptr_t)rhs, r1 = r0 + (uintptr_t)(5 * nelem * Np * 8);
+    const uintptr_t in[4][2] = {{(uintptr_t)q, (uintptr_t)q + (uintptr_t)(5 * nelem * Np * 8)},
+                                {(uintptr_t)phi, (uintptr_t)phi + (uintptr_t)(nelem * Np * 8)},
+                                {(uintptr_t)geom, (uintptr_t)geom + (uintptr_t)(10 * nelem * Np * 8)},
+                                {(uintptr_t)D, (uintptr_t)D + (uintptr_t)((N + 1) * (N + 1) * 8)}};
+    for (int i = 0; i < 4; ++i)
+        if (r0 < in[i][1] && in[i][0] < r1) return ESDG_ERR_ALIAS;
+    const esdg::Rotation<double> rot{0.0, 0.0, 0.0, false};
+    const esdg::Sink<double, false> sink{rhs, nullptr, 0.0, 0.0, 0.0};
+    if (N == 5)
+        hipLaunchKernelGGL((esdg::volume_rhs_kernel<double, 5, C5>), dim3((unsigned)nelem),
+                           dim3(C5::NT), 0, stream, q, nullptr, phi, geom, D, nullptr, rot, nelem,
+                           sink);
+    else
+        hipLaunchKernelGGL((esdg::volume_rhs_kernel<double, 7, C7>), dim3((unsigned)nelem),
+                           dim3(C7::NT), 0, stream, q, nullptr, phi, geom, D, nullptr, rot, nelem,
+                           sink);
+    return hipGetLastError() == hipSuccess ? ESDG_OK : ESDG_ERR_LAUNCH;
+}
+
 const char *esdg_ablation_name(int variant)
 {
     if (variant & ESDG_ABL_FUSE_FLAG) {

@@ -173,7 +173,8 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 // thread.
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
           int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
-          int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0>
+          int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0,
+          int LANES_ = 1>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -205,6 +206,9 @@ struct LaunchCfg {
     static constexpr int kPlanePad = PLANE_PAD_;
     static constexpr int kElemPad = ELEM_PAD_;
     static constexpr int WAVES_SURF = WAVES_SURF_;
+    // LANES = 2: two adjacent lanes share a line, each owning half its nodes
+    // (line_pairs_x2); otherwise one lane per line.
+    static constexpr int kLanes = LANES_;
 };
 
 template <int N, class C>
@@ -222,7 +226,12 @@ struct Shape {
     static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
     // thread-index stride between the directions' first line tasks
     static constexpr int kDirStride = C::kDirAligned ? (C::EPB * Nq2 + 31) / 32 * 32 : C::EPB * Nq2;
-    static constexpr int kTaskThreads = C::kDirMajor ? 3 * kDirStride : kLines;
+    static constexpr int kTaskThreads = C::kLanes * (C::kDirMajor ? 3 * kDirStride : kLines);
+    // nodes of a line each lane owns
+    static constexpr int kOwn = Nq / C::kLanes;
+    static_assert(C::kLanes == 1 || (C::kLanes == 2 && Nq % 2 == 0 && !C::kMetricInLds &&
+                                     !C::kCacheLine),
+                  "two lanes per line: an even node count, the line metric in registers");
     static constexpr int kNodeIters = (kNodes + C::NT - 1) / C::NT;  // nodes per thread
     static constexpr int kStaged = C::kMetricInLds ? kNodeValues : kJa;
     static constexpr int kPartials = C::kFinalizeInLine ? 10 : kPartialValues;
@@ -405,9 +414,11 @@ struct LineTask {
     // nb, step: LDS slot of the line's first node and the slot stride along
     // the line; n0, nstep: the same in the node numbering of one element
     int eb, k, nb, step, n0, nstep;
+    int half;  // which half of the line's nodes this lane owns (two lanes per line)
     __device__ inline LineTask() {
         constexpr int Nq = S::Nq, Nq2 = S::Nq2, Np = S::Np;
-        const int task = threadIdx.x;
+        const int task = (int)threadIdx.x / C::kLanes;
+        half = (int)threadIdx.x % C::kLanes;
         int line;
         if constexpr (C::kDirMajor) {
             k = task / S::kDirStride;
@@ -457,6 +468,12 @@ struct LineTask {
     __device__ inline bool active(int nvalid) const {
         return (int)threadIdx.x < S::kTaskThreads && eb * S::Np < nvalid;
     }
+    // Two lanes per line: the lane with half 0 owns line nodes 0..kOwn-1 as
+    // its local nodes 0..kOwn-1, the lane with half 1 owns N..N-kOwn+1 (its
+    // local node j is line node N - j).  own(j) / other(j): the line index of
+    // this lane's / the other lane's local node j.
+    __device__ inline int own(int j) const { return half ? N - j : j; }
+    __device__ inline int other(int j) const { return half ? j : N - j; }
 };
 
 // Global values one thread loads for phase A: IT nodes x (5 fields, phi,
@@ -759,6 +776,194 @@ __device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const L
         line_pairs_form<T, N, C, false>(lds, D, L, lm, acc);
 }
 
+// ---------------------------------------------------------------------------
+// Two lanes per line (LANES = 2, an even node count Nq = 2H).  Adjacent lanes
+// 2t and 2t+1 share a line; each owns H of its nodes (LineTask::own) and
+// holds only their accumulators and metric, about half the registers of a
+// whole line.  Every unordered pair of the line is evaluated once, except the
+// H pairs (j, N-j) that join the two halves' mirror nodes, which both lanes
+// evaluate at half weight:
+//   * pairs within a half: by the owning lane, both contributions local;
+//   * pairs across the halves, for each local index y of the other lane:
+//     pairs (own x, other y) with x <= y.  The lane with half 0 covers the
+//     line pairs (x, N-y), x <= y; the lane with half 1 the pairs (N-x, y),
+//     x <= y, i.e. (x', N-y') with x' >= y': together every cross pair once,
+//     the mirror pairs x = y twice.  The partner's contributions are summed
+//     in registers over x and handed to the other lane once per y, with the
+//     partner's metric, by a DPP swap of adjacent lanes.
+// The LGL differentiation matrix satisfies D[N-a][N-l] = -D[a][l], so the
+// coefficients of the lane with half 1 are those of the lane with half 0 at
+// the same local indices with the opposite sign: both lanes read the same
+// (uniform) D values, and the lane with half 1 keeps its accumulators
+// negated, which it undoes when it writes them (line_sign).  What a lane
+// receives from the other is therefore always subtracted.
+
+// The value of the adjacent lane (2t <-> 2t+1): DPP quad_perm [1, 0, 3, 2].
+__device__ inline float swap_lanes(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1,
+                                                             0xF, 0xF, false));
+}
+__device__ inline double swap_lanes(double x)
+{
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, 0xB1, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), 0xB1, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// +1 for the lane with half 0, -1 for the one with half 1 (see above).
+template <typename T, int N, class C>
+__device__ inline T line_sign(const LineTask<N, C> &L)
+{
+    return L.half ? T(-1) : T(1);
+}
+
+template <typename T, int N, class C, bool SERIES>
+__device__ inline void line_pairs_x2_form(const T *lds, const T *__restrict__ D,
+                                          const LineTask<N, C> &L, const T (&lm)[(N + 1) / 2][3],
+                                          T (&acc)[(N + 1) / 2][5])
+{
+    constexpr int Nq = N + 1, H = Nq / 2, SLOTS = Shape<N, C>::kSlots;
+    // pairs within the own half
+#pragma unroll
+    for (int x = 0; x < H - 1; ++x) {
+        asm volatile("" ::: "memory");
+        NodeRegs<T> X;
+        X.load_state(lds, SLOTS, L.nb + L.own(x) * L.step);
+        X.n1 = lm[x][0]; X.n2 = lm[x][1]; X.n3 = lm[x][2];
+#pragma unroll
+        for (int y = x + 1; y < H; ++y) {
+            NodeRegs<T> Y;
+            Y.load_state(lds, SLOTS, L.nb + L.own(y) * L.step);
+            Y.n1 = lm[y][0]; Y.n2 = lm[y][1]; Y.n3 = lm[y][2];
+            pair_update<T, SERIES>(X, Y, D + x * Nq + y, D + y * Nq + x, acc[x], acc[y]);
+        }
+    }
+    // pairs across the halves
+#pragma unroll
+    for (int y = 0; y < H; ++y) {
+        asm volatile("" ::: "memory");
+        NodeRegs<T> P;
+        P.load_state(lds, SLOTS, L.nb + L.other(y) * L.step);
+        P.n1 = swap_lanes(lm[y][0]);
+        P.n2 = swap_lanes(lm[y][1]);
+        P.n3 = swap_lanes(lm[y][2]);
+        T pacc[5] = {T(0), T(0), T(0), T(0), T(0)};
+#pragma unroll
+        for (int x = 0; x <= y; ++x) {
+            NodeRegs<T> X;
+            X.load_state(lds, SLOTS, L.nb + L.own(x) * L.step);
+            X.n1 = lm[x][0]; X.n2 = lm[x][1]; X.n3 = lm[x][2];
+            if (x == y) {
+                // the mirror pair (x, N-x): both lanes evaluate it, each at half weight
+                const T dal = T(0.5) * D[x * Nq + (N - y)];
+                const T dla = T(0.5) * D[(N - y) * Nq + x];
+                pair_update<T, SERIES>(X, P, &dal, &dla, acc[x], pacc);
+            } else {
+                pair_update<T, SERIES>(X, P, D + x * Nq + (N - y), D + (N - y) * Nq + x, acc[x],
+                                       pacc);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 5; ++f) acc[y][f] -= swap_lanes(pacc[f]);
+    }
+}
+
+template <typename T, int N, class C, bool SPLIT>
+__device__ inline void line_pairs_x2(const T *lds, const T *__restrict__ D, const LineTask<N, C> &L,
+                                     const T (&lm)[(N + 1) / 2][3], T (&acc)[(N + 1) / 2][5])
+{
+    if (SPLIT && __all(line_in_series<T, N, C>(lds, L)))
+        line_pairs_x2_form<T, N, C, true>(lds, D, L, lm, acc);
+    else
+        line_pairs_x2_form<T, N, C, false>(lds, D, L, lm, acc);
+}
+
+// The face neighbour of the one line end a lane owns (its local node 0: line
+// node 0 for half 0, N for half 1).
+template <typename T, bool PERT = false>
+struct FaceLoad1 {
+    int32_t nb;
+    T v[PERT ? 8 : 6];
+    __device__ inline void issue_neighbour(const int32_t *__restrict__ nbr, int64_t e, int k,
+                                           int end) {
+        nb = nbr[6 * e + 2 * k + end];
+    }
+    template <int N>
+    __device__ inline void issue_state(const T *__restrict__ q, const T *__restrict__ ref,
+                                       const T *__restrict__ phi, int64_t fstride, int64_t nelem,
+                                       int local0, int step, int end) {
+        constexpr int Np = (N + 1) * (N + 1) * (N + 1);
+        if (nb >= 0 && nb < nelem) {
+            const int64_t g = (int64_t)nb * Np + local0 + (end == 0 ? N : 0) * step;
+#pragma unroll
+            for (int f = 0; f < 5; ++f) v[f] = q[f * fstride + g];
+            v[5] = phi[g];
+            if constexpr (PERT) {
+                v[6] = ref[g];
+                v[7] = ref[fstride + g];
+            }
+        }
+    }
+    __device__ inline NodeRegs<T> partner() const {
+        if constexpr (PERT)
+            return node_values<T, true>(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+        else
+            return node_values(v[0], v[1], v[2], v[3], v[4], v[5]);
+    }
+};
+
+// Surface term of the owned line end (see surface_ends).  The owned end's
+// coefficient is -N(N+1)/4 on the -xi_k face (half 0) and +N(N+1)/4 on the
+// +xi_k face (half 1), whose accumulators are kept negated: -N(N+1)/4 for both.
+template <typename T, int N, class C, bool PERT>
+__device__ inline void surface_end_x2(const T *lds, const LineTask<N, C> &L,
+                                      const T (&lm)[(N + 1) / 2][3], const FaceLoad1<T, PERT> &F,
+                                      int64_t nelem, T (&acc)[(N + 1) / 2][5])
+{
+    using A = Arith<T>;
+    constexpr int SLOTS = Shape<N, C>::kSlots;
+    constexpr double kEnd = N * (N + 1) / 4.0;
+    NodeRegs<T> X;
+    X.load_state(lds, SLOTS, L.nb + L.own(0) * L.step);
+    X.n1 = lm[0][0]; X.n2 = lm[0][1]; X.n3 = lm[0][2];
+    NodeRegs<T> Y = X;
+    if (F.nb == kFaceWall) {
+        const T nn = X.n1 * X.n1 + X.n2 * X.n2 + X.n3 * X.n3;
+        const T un2 = T(2) * (X.u1 * X.n1 + X.u2 * X.n2 + X.u3 * X.n3) * A::rcp(nn);
+        Y.u1 = X.u1 - un2 * X.n1;
+        Y.u2 = X.u2 - un2 * X.n2;
+        Y.u3 = X.u3 - un2 * X.n3;
+    } else if (F.nb >= 0 && F.nb < nelem) {
+        Y = F.partner();
+        Y.n1 = X.n1; Y.n2 = X.n2; Y.n3 = X.n3;
+    } else {
+        Y.rho = T(__builtin_nan(""));  // invalid neighbour index: the result says so
+    }
+    const T coef = T(-kEnd);
+    T partner[5] = {T(0), T(0), T(0), T(0), T(0)};
+    pair_update(X, Y, &coef, &coef, acc[0], partner);
+}
+
+// Phase C with two lanes per line: each lane writes its own nodes' partials
+// (sign restored).
+template <typename T, int N, class C>
+__device__ inline void write_partials_x2(T *lds, const LineTask<N, C> &L, bool active,
+                                         const T (&acc)[(N + 1) / 2][5])
+{
+    constexpr int SLOTS = Shape<N, C>::kSlots;
+    if (active && (!C::kFinalizeInLine || L.k < 2)) {
+        const T sg = line_sign<T>(L);
+#pragma unroll
+        for (int j = 0; j < (N + 1) / 2; ++j) {
+            const int s = L.nb + L.own(j) * L.step;
+#pragma unroll
+            for (int f = 0; f < 5; ++f) lds[(L.k * 5 + f) * SLOTS + s] = sg * acc[j][f];
+        }
+    }
+}
+
 // Source term h of the whole right-hand side: the Coriolis term of the
 // momentum equation, h = -omega x U (U the momentum).  `on` is uniform over
 // the launch; the momentum is re-read at the store (the workgroup loaded it
@@ -856,6 +1061,31 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
     }
 }
 
+// FIN with two lanes per line: a direction-3 lane finishes its own nodes.
+template <typename T, int N, class C, bool STAGE>
+__device__ inline void finish_line_x2(const T *lds, const LineTask<N, C> &L, bool active,
+                                      const Batch<N, C> &B, int64_t fstride,
+                                      const T (&acc)[(N + 1) / 2][5], const T *__restrict__ q,
+                                      const Rotation<T> &rot, const Sink<T, STAGE> &sink)
+{
+    constexpr int SLOTS = Shape<N, C>::kSlots;
+    if (active && L.k == 2) {
+        const T sg = line_sign<T>(L);
+#pragma unroll
+        for (int j = 0; j < (N + 1) / 2; ++j) {
+            const int a = L.own(j);
+            const int s = L.nb + a * L.step;
+            const T mJ = lds[Shape<N, C>::kMinusInvJ * SLOTS + s];
+            const int64_t g = B.g0 + L.node(a);
+            T r[5];
+#pragma unroll
+            for (int f = 0; f < 5; ++f)
+                r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + sg * acc[j][f]) * mJ;
+            sink.put(q, fstride, g, rot, r);
+        }
+    }
+}
+
 template <typename T, int N, class C, bool STAGE>
 __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fstride,
                                  const T (&mJ)[Shape<N, C>::kNodeIters], const T *__restrict__ q,
@@ -906,6 +1136,53 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     if constexpr (!SURF) rot.on = false;  // the volume term alone has no source
 
     // phase A: issue every global load first
+    if constexpr (C::kLanes == 2) {
+        constexpr int H = Nq / 2;
+        FaceLoad1<T, PERT> face;
+        if constexpr (SURF) {
+            if (active) face.issue_neighbour(nbr, batch * C::EPB + L.eb, L.k, L.half);
+        }
+        NodeLoads<T, N, C, PERT> ld;
+        ld.issue(q, ref, phi, geom, fstride, B);
+        T lm[H][3];
+        if (active) {
+#pragma unroll
+            for (int j = 0; j < H; ++j)
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    lm[j][c] = geom[(3 * L.k + c) * fstride + B.g0 + L.node(L.own(j))];
+        }
+        if constexpr (SURF) {
+            if (active) face.template issue_state<N>(q, ref, phi, fstride, nelem,
+                                                    L.first_in_element(), L.node_step(), L.half);
+        }
+        T mJ[S::kNodeIters];
+        stage_nodes<T, N, C, PERT>(ld, B, lds, mJ);
+        __syncthreads();
+
+        // phase B
+        T acc[H][5];
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+#pragma unroll
+            for (int f = 0; f < 5; ++f) acc[j][f] = T(0);
+        if constexpr (SURF) {
+            if (active) surface_end_x2<T, N, C, PERT>(lds, L, lm, face, nelem, acc);
+        }
+        constexpr bool kSplit = SURF ? C::kSeriesFormSurf : C::kSeriesForm;
+        if (active) line_pairs_x2<T, N, C, kSplit>(lds, D, L, lm, acc);
+        __syncthreads();
+
+        // phases C, D
+        write_partials_x2<T, N, C>(lds, L, active, acc);
+        __syncthreads();
+        if constexpr (C::kFinalizeInLine) {
+            finish_line_x2<T, N, C, STAGE>(lds, L, active, B, fstride, acc, q, rot, sink);
+        } else {
+            store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
+        }
+        return;
+    } else {
     FaceLoads<T, PERT> face;
     if constexpr (SURF) {
         if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
@@ -951,6 +1228,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         finish_line<T, N, C, STAGE>(lds, L, active, B, fstride, acc, q, rot, sink);
     } else {
         store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
+    }
     }
 }
 

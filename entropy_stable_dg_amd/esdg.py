@@ -22,7 +22,7 @@ ESDG_ERR_ORDER = -2
 ESDG_ERR_NELEM = -3
 ESDG_ERR_LAUNCH = -4
 ESDG_ERR_ALIAS = -5
-ESDG_ERR_DEVICE = -6
+ESDG_ERR_DEVICE = -7
 
 # every symbol include/esdg.h declares
 EXPORTS = ("esdg_volume_rhs_f64", "esdg_volume_rhs_f32", "esdg_rhs_f64", "esdg_rhs_f32",

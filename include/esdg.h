@@ -60,7 +60,7 @@ extern "C" {
 #define ESDG_ERR_NELEM  (-3)  /* nelem < 0, or the arrays would not be addressable  */
 #define ESDG_ERR_LAUNCH (-4)  /* the kernel launch failed (hipGetLastError)         */
 #define ESDG_ERR_ALIAS  (-5)  /* an output overlaps an input or another output      */
-#define ESDG_ERR_DEVICE (-6)  /* the current device (or its scratch array) could not
+#define ESDG_ERR_DEVICE (-7)  /* the current device (or its scratch array) could not
                                  be located: esdg_integrals_noalloc_f64 only          */
 
 /* Volume term in fp64 arithmetic. Returns a status code above. */

@@ -64,6 +64,22 @@ int esdg_ablation_volume_rhs_f64(int variant, const double *q, const double *phi
                                  const double *geom, const double *D, int N, int64_t nelem,
                                  double *rhs, hipStream_t stream);
 
+/*
+ * The production kernel of esdg_volume_rhs_f64 with two lanes per grid line
+ * instead of one, at N = 5 and N = 7 (ESDG_ERR_ORDER otherwise): adjacent
+ * lanes each own half of a line's nodes, evaluate the pairs within their
+ * half and half of the pairs across the halves, and hand the partner's
+ * contributions to the other lane by a cross-lane (DPP) swap, so a lane holds
+ * half the accumulators and metric of a line and the kernel fits three waves
+ * per SIMD instead of two.  It is kept for measurement against the
+ * one-lane-per-line production shape (same result up to rounding, same
+ * contract as esdg_volume_rhs_f64); the page's register-pressure remark
+ * ([ESDG-GPU §4.1], temporary local copies and occupancy) is what it tests.
+ */
+int esdg_ablation_two_lane_volume_rhs_f64(const double *q, const double *phi, const double *geom,
+                                          const double *D, int N, int64_t nelem, double *rhs,
+                                          hipStream_t stream);
+
 /* Short name of a variant, with or without ESDG_ABL_FUSE_FLAG (static
  * string, "unknown" outside the list). */
 const char *esdg_ablation_name(int variant);

@@ -24,10 +24,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "esdg_api.hip")
 
 # LaunchCfg<EPB, NT, WAVES, METRIC_LDS, CACHE, KMAJOR, FIN, SERIES, SERIES_SURF,
-#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF> and its defaults
+#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES> and its defaults
 FIELDS = ("epb", "nt", "waves", "metric_lds", "cache", "kmajor", "fin", "series", "series_surf",
-          "row_pad", "plane_pad", "elem_pad", "waves_surf")
-DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+          "row_pad", "plane_pad", "elem_pad", "waves_surf", "lanes")
+DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1)
 
 # staged values per node (without / with the metric) and partial sums per node
 STAGED_NO_METRIC, STAGED_WITH_METRIC = 10, 19
@@ -72,7 +72,8 @@ class Shape:
         self.lines = 3 * self.EPB * self.Nq2
         lines_per_dir = self.EPB * self.Nq2
         self.dir_stride = (lines_per_dir + 31) // 32 * 32 if c["kmajor"] == 2 else lines_per_dir
-        self.task_threads = 3 * self.dir_stride if c["kmajor"] else self.lines
+        self.lanes = c.get("lanes", 1)
+        self.task_threads = self.lanes * (3 * self.dir_stride if c["kmajor"] else self.lines)
         staged = STAGED_WITH_METRIC if c["metric_lds"] else STAGED_NO_METRIC
         partials = PARTIALS_FIN if c["fin"] else PARTIALS
         self.region = max(staged, partials) + (1 if c["fin"] else 0)
@@ -85,9 +86,14 @@ class Shape:
         y, x = divmod(r2, self.Nq)
         return e * self.E + z * self.P + y * self.R + x
 
+    def half(self, thread: int) -> int:
+        """Which half of its line a thread owns (0 with one lane per line)."""
+        return thread % self.lanes
+
     def task(self, thread: int):
         """(e, k, line) of a thread's line task, as the kernel derives it."""
         Nq2, EPB = self.Nq2, self.EPB
+        thread //= self.lanes
         if self.cfg["kmajor"]:
             k, r = divmod(thread, self.dir_stride)
             e, line = divmod(r, Nq2)
@@ -128,7 +134,8 @@ def bank_cost(shape: Shape, words: int, banks: int) -> tuple:
                 if thread >= shape.NT or not shape.active(thread, shape.EPB):
                     continue
                 n += 1
-                s = shape.line_nodes(*shape.task(thread))[1][0]
+                slots = shape.line_nodes(*shape.task(thread))[1]
+                s = slots[-1] if shape.half(thread) else slots[0]
                 for d in range(words * s, words * s + words):
                     per_bank.setdefault(d % banks, set()).add(d)
             if n:

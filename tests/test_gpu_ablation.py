@@ -82,3 +82,31 @@ def test_ladder_at_the_timed_size():
         del out
     del big
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N", abl.TWO_LANE_ORDERS)
+def test_two_lane_variant_parity(N):
+    """Two lanes per line with the cross-lane exchange (N = 5, 7): every
+    order it covers on a random warped mesh, a ragged count and the N = 7
+    high-order workload, against the oracle."""
+    q, phi, geom, D = random_workload(N, nelem_xyz=(3, 2, 2), seed=90 + N)
+    tq, tp, tg, tD = to_gpu(q, phi, geom, D)
+    got = abl.two_lane_volume_rhs(tq, tp, tg, tD)
+    torch.cuda.synchronize()
+    check(got.cpu().numpy(), oracle.volume_rhs(q, phi, geom, D, N), TOL[np.float64],
+          f"two lanes N={N}")
+    ne = 5
+    got = abl.two_lane_volume_rhs(tq[:, :ne].contiguous(), tp[:ne].contiguous(),
+                                  tg[:, :ne].contiguous(), tD)
+    torch.cuda.synchronize()
+    check(got.cpu().numpy(), oracle.volume_rhs(q[:, :ne], phi[:ne], geom[:, :ne], D, N),
+          TOL[np.float64], f"two lanes N={N} {ne} elements")
+
+
+def test_two_lane_variant_high_order_workload():
+    wl = I.make("high_order")
+    tq, tp, tg, tD = to_gpu(wl.q, wl.phi, wl.geom, wl.D)
+    got = abl.two_lane_volume_rhs(tq, tp, tg, tD)
+    torch.cuda.synchronize()
+    check(got.cpu().numpy(), oracle.volume_rhs(wl.q, wl.phi, wl.geom, wl.D, wl.N),
+          TOL[np.float64], "two lanes, high order")

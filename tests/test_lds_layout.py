@@ -36,9 +36,13 @@ def test_every_line_once_also_in_a_ragged_workgroup(dtype, N):
             if s.active(thread, nvalid):
                 e, k, line = s.task(thread)
                 assert 0 <= k <= 2 and 0 <= line < s.Nq2 and 0 <= e < nvalid
-                seen.append((e, k, line))
-        assert sorted(seen) == sorted((e, k, line) for e in range(nvalid) for k in range(3)
-                                      for line in range(s.Nq2))
+                seen.append((e, k, line, s.half(thread)))
+        # each line once per lane, the lanes of a line adjacent
+        assert sorted(seen) == sorted((e, k, line, h) for e in range(nvalid) for k in range(3)
+                                      for line in range(s.Nq2) for h in range(s.lanes))
+        if s.lanes == 2:
+            for thread in range(0, s.task_threads, 2):
+                assert s.task(thread) == s.task(thread + 1)
 
 
 @pytest.mark.parametrize("dtype,N", CASES)
@@ -70,7 +74,7 @@ def test_bank_model_sees_the_power_of_two_conflict():
     # N = 7, one element, direction-major: unpadded, direction-1 lines start
     # 64 bytes apart, so a 64-bank wave pays several times the
     # conflict-free cycles; one pad value per row brings it near one
-    cfg = dict(zip(L.FIELDS, (1, 192, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0)))
+    cfg = dict(zip(L.FIELDS, (1, 192, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0, 1)))
     plain = L.bank_cost(L.Shape(7, cfg), 2, 64)
     padded = L.bank_cost(L.Shape(7, dict(cfg, row_pad=1)), 2, 64)
     assert plain[0] >= 4 * plain[1]
