@@ -34,7 +34,10 @@ constexpr int kMaxOrder = 8;
 // 64-lane boundary (order 2), at the same 192 threads.  Other pads and orders were neutral
 // to slower.  At fp64 N = 5 a 3-wave register cap on the volume kernel (168
 // registers, a 36-byte spill) lets three workgroups share a CU instead of
-// two; at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
+// two; the kernel with the surface term at fp64 N = 3, 4 and 6 carries the
+// series form under a 3-wave cap (no spill at N = 3, 108 and 28 bytes at
+// N = 4 and 6; 2-10 % faster than the general form alone, while at N = 5 the
+// same cap spills 244 bytes and runs 1.4x slower); at fp32 N = 4 and 5 a 5-wave cap on the kernel with the surface term
 // (96 and 89 registers) does the same for five workgroups instead of four,
 // and at fp32 N = 7 and 8 direction-3 lines that finish their nodes (25 and
 // 32 KB of LDS) with 4-wave caps (128 registers) give five and four
@@ -47,10 +50,10 @@ template <typename T, int N> struct Launch;
 // pad per row, per plane, per element, waves hint with the surface term>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };     // 189/192
-template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, false, 0, 3>; };          // 192/192
-template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true>; };           // 225/256
+template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, true, 0, 3, 0, 3>; };          // 192/192
+template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 3>; };           // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 3, false, false, true, false, true, true>; };    // 216/256
-template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, 2, false, true>; };          // 147/192
+template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, 2, false, true, true, 0, 0, 0, 3>; };          // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192
 template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true>; };                 // 243/256
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
