@@ -358,16 +358,23 @@ static void add_coriolis_r(const real *q, const double omega[3], int64_t nnodes,
     }
 }
 
-/* double <-> real copies of whole arrays */
+/* double <-> real copies of whole arrays (split over the OpenMP threads, so
+ * that the copies of the long double build do not serialise a call) */
 static real *promote(const double *x, int64_t n)
 {
     real *r = (real *)calloc((size_t)(n > 0 ? n : 1), sizeof(real));
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
     for (int64_t i = 0; i < n; ++i) r[i] = x[i];
     return r;
 }
 
 static void demote(const real *r, int64_t n, double *x)
 {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
     for (int64_t i = 0; i < n; ++i) x[i] = (double)r[i];
 }
 
