@@ -276,9 +276,15 @@ def time_stages(name: str, steps: int, warmup: int, rotate_bytes: float, pert: b
     log(f"{name} stage{' (perturbation variables)' if pert else ''}: {sec * 1e6:.2f} us/stage")
     del sets
     torch.cuda.empty_cache()
+    from entropy_stable_dg_amd import perfmodel
+
+    nbytes = perfmodel.algorithmic_bytes_stage(wl.N, wl.nelem, dtype)
+    if pert:
+        nbytes += 2 * wl.dof * (8 if dtype == "f64" else 4)
     return sec, {"N": wl.N, "nelem": wl.nelem, "dof": wl.dof, "dtype": dtype, "dt": dt,
                  "stages_timed": 10 * calls, "buffer_sets": nsets, "preroll_passes": passes,
-                 "state_finite_after": finite}
+                 "state_finite_after": finite, "bytes_per_stage": nbytes,
+                 "hbm_gbs_algorithmic": nbytes / sec / 1e9}
 
 
 def conservation_drift(name: str, nsteps: int, pert: bool = False) -> dict:
@@ -335,6 +341,11 @@ def profile_pass(steps: int, workload: str = HEADLINE) -> dict:
     torch.cuda.synchronize()
     del src, dst
     name, _, mode = workload.partition(":")
+    if mode in ("stage", "stage_pert"):
+        sec, inf = time_stages(name, 10 * steps, 10, 512e6, pert=(mode == "stage_pert"))
+        return {"profile_pass": True, "workload": workload, "copy_bytes_each_way": n * 8,
+                "us_per_stage": sec * 1e6, "bytes_per_launch": inf["bytes_per_stage"],
+                "kernel_source_hash": kernel_source_hash()}
     cold, hot, info, _ = time_workload(name, steps, 2, 512e6, full=(mode == "rhs"),
                                        two_lane=(mode == "two_lane"))
     return {"profile_pass": True, "workload": workload, "copy_bytes_each_way": n * 8,
@@ -607,7 +618,8 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE,
                     help="workload of the profile pass (tiny, bubble, baroclinic, bubble_f32, "
                          "high_order; a ':rhs' suffix profiles the whole right-hand side, "
-                         "':two_lane' the two-lanes-per-line variant)")
+                         "':two_lane' the two-lanes-per-line variant, ':stage' the fused "
+                         "Runge-Kutta stage, ':stage_pert' the same in perturbation variables)")
     ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,high_order,"
                                        "high_order:two_lane",
                     help="comma-separated extra workloads to time (reported under 'extra'); "

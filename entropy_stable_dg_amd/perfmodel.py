@@ -139,3 +139,13 @@ def face_partner_bytes(N: int, nbr, dtype: str) -> int:
 
 def algorithmic_bytes_rhs(N: int, nelem: int, dtype: str) -> int:
     return algorithmic_bytes(N, nelem, dtype) + 24 * nelem
+
+
+def algorithmic_bytes_stage(N: int, nelem: int, dtype: str) -> float:
+    """Bytes of one fused Runge-Kutta stage, averaged over the five stages of
+    a step: the whole right-hand side's inputs (16 values per node and the
+    connectivity), the register dq read (by four of the five stages: the
+    first does not read it) and written, and the next state written: 16 +
+    4/5 x 5 + 10 = 30 values per node."""
+    size = 8 if dtype == "f64" else 4
+    return nelem * (N + 1) ** 3 * 30 * size + (N + 1) ** 2 * size + 24 * nelem
