@@ -689,7 +689,7 @@ def main() -> int:
             "traffic": measured_traffic(key.replace(":", "_"), inf["dtype"]),
             "gflops_counted_fp64": (lambda fl: fl / c / 1e9 if fl else None)(
                 counted_fp64_flops(key.replace(":", "_"), inf["dtype"])),
-            "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"],
+            "dtype": inf["dtype"], "N": inf["N"], "nelem": inf["nelem"], "preroll": inf["preroll"],
             "hbm_frac": inf["bytes"] / c / 1e9 / perfmodel.PEAK_HBM_GBS,
             "frac_fp64_vector_peak": (inf["flops"] / c / 1e12 / perfmodel.PEAK_FP64_VECTOR_TFLOPS
                                       if inf["dtype"] == "f64" else None),
@@ -783,6 +783,8 @@ def main() -> int:
         "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
         "hot_ms_per_step": t_hot * 1e3,
         "hot_dof_per_s": info["dof"] / t_hot,
+        # untimed launches run before each timed pass (warm device whatever the host did before)
+        "preroll": info["preroll"],
         "kernel_source_hash": kernel_source_hash(),
         "hbm_stream81_gbs": stream_gbs,
         "hbm_stream81_gbs_by_lane_width": {"8B": stream_narrow, "32B": stream_wide},
