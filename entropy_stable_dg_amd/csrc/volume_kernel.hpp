@@ -54,6 +54,12 @@
 // element (or the mirror state at a slip wall) to that end's accumulator
 // ([ESDG-GPU §3, Eq. 2], surface part); the Coriolis source of Eq. 1b is
 // added at the store.
+//
+// On perturbation variables in fp32 (the page's cure for 32-bit noise,
+// [ESDG-GPU §5.2]) the momentum flux's pressure mean is formed relative to
+// each element's reference pressure, and the constant part is added once per
+// line node in fp64 (pressure_reference): the same values in exact
+// arithmetic, with the O(p) rounding of every pair taken out.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -238,7 +244,14 @@ struct Shape {
     static constexpr int kRegion = kStaged > kPartials ? kStaged : kPartials;
     // with FIN, -1/J of every node is staged after the shared region
     static constexpr int kMinusInvJ = kRegion;
-    static constexpr int kLdsValues = (kRegion + (C::kFinalizeInLine ? 1 : 0)) * kSlots;
+    static constexpr int kFixedValues = kRegion + (C::kFinalizeInLine ? 1 : 0);
+    // The split pressure (pressure_reference below) stages one more value per
+    // node, b (p - P): inside the shared region when the partials leave a
+    // value free there, else after everything else.
+    static constexpr int kBDelta = kStaged < kPartials ? kStaged : kFixedValues;
+    template <bool PSPLIT>
+    static constexpr int kLdsValues =
+        (kFixedValues + (PSPLIT && kBDelta == kFixedValues ? 1 : 0)) * kSlots;
     static_assert(kTaskThreads <= C::NT, "one line task per thread");
     static_assert(!C::kDirAligned || C::kDirMajor, "aligned order is direction-major");
     static_assert(C::kRowPad >= 0 && C::kPlanePad >= 0 && C::kElemPad >= 0, "pads");
@@ -259,6 +272,7 @@ struct Shape {
 template <typename T>
 struct NodeRegs {
     T rho, u1, u2, u3, b, lrho, lb, ph, w, ib, n1, n2, n3;
+    T bd;  // b (p - P) for the split pressure (pressure_reference)
     __device__ inline void load_state(const T *lds, int SLOTS, int s) {
         rho = lds[kRho * SLOTS + s];
         u1 = lds[kU1 * SLOTS + s];
@@ -270,6 +284,9 @@ struct NodeRegs {
         ph = lds[kPhi * SLOTS + s];
         w = lds[kW * SLOTS + s];
         ib = lds[kInvB * SLOTS + s];
+    }
+    __device__ inline void load_bd(const T *lds, int SLOTS, int s, int index) {
+        bd = lds[index * SLOTS + s];
     }
     __device__ inline void load_metric(const T *lds, int SLOTS, int s, int k) {
         n1 = lds[(kJa + 3 * k + 0) * SLOTS + s];
@@ -297,10 +314,13 @@ __device__ inline T two_atanh_over_s(T f)
 // X and Y are taken by value: a reference would take the address of the
 // caller's locals, and the compiler fence in the pair loop would then keep
 // them in scratch memory.  D[a][l] and D[l][a] are read where they are used.
-template <typename T, bool SERIES = false>
+// PSPLIT: the momentum flux takes the pressure mean relative to the
+// element's reference pressure P (pressure_reference), from the staged
+// b (p - P); the energy flux keeps its whole pressure mean.
+template <typename T, bool SERIES = false, bool PSPLIT = false>
 __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
                                    const T *__restrict__ Dal_p, const T *__restrict__ Dla_p,
-                                   T *acc_a, T *acc_l)
+                                   T *acc_a, T *acc_l, T P = T(0))
 {
     using A = Arith<T>;
     const T eps = T(A::kSeries);
@@ -343,21 +363,25 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
         const T tb = db * isb;
         iLb = select(ser_b, two_atanh_over_s(tb * tb) * isb, lnk * (Y.lb - X.lb) * iBb);
     }
-    // {{rho}}/(2{{b}}) with the b scaling undone
-    const T pt = half_bscale * sr * isb;
+    // {{rho}}/(2{{b}}) with the b scaling undone; split: {{rho}}/(2{{b}}) - P
+    // = (b_a (p_a - P) + b_l (p_l - P)) / (b_a + b_l)
+    const T pt = PSPLIT ? (X.bd + Y.bd) * isb : half_bscale * sr * isb;
     // metric of the pair: Ja^k(a) + Ja^k(l); {{u}} (staged u is halved)
     const T c1 = X.n1 + Y.n1, c2 = X.n2 + Y.n2, c3 = X.n3 + Y.n3;
     const T s1 = X.u1 + Y.u1, s2 = X.u2 + Y.u2, s3 = X.u3 + Y.u3;
     // contravariant density flux {{rho}}_log ({{u}} . c)
-    const T Fr = Lr * (c1 * s1 + c2 * s2 + c3 * s3);
+    const T cs = c1 * s1 + c2 * s2 + c3 * s3;
+    const T Fr = Lr * cs;
     // symmetric momentum part S~_m = F~rho {{u_m}} + c_m {{rho}}/(2{{b}})
     const T S1 = fma(Fr, s1, c1 * pt);
     const T S2 = fma(Fr, s2, c2 * pt);
     const T S3 = fma(Fr, s3, c3 * pt);
     // energy: (1/(2(g-1){{b}}_log) - {{|u|^2}}/2 + {{phi}}) F~rho + {{u}} . S~,
     // with -{{|u|^2}}/2 + {{phi}} = {{w}} (staged w is halved)
+    // (split: S~ lacks c P, so {{u}} . S~ lacks P ({{u}} . c), added back here)
     const T coef = fma(cE, iLb, X.w + Y.w);
-    const T FE = fma(coef, Fr, s1 * S1 + s2 * S2 + s3 * S3);
+    const T uS = s1 * S1 + s2 * S2 + s3 * S3;
+    const T FE = fma(coef, Fr, PSPLIT ? fma(P, cs, uS) : uS);
     // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
     // = (s_b b_a + s_b b_l) {{rho}}_log [[phi/4]] / (s_b b_own)  (staged phi is phi/4)
     const T g = sb * Lr * (Y.ph - X.ph);
@@ -476,14 +500,18 @@ struct LineTask {
     __device__ inline int other(int j) const { return half ? j : N - j; }
 };
 
+// The node whose reference pressure is its element's P (pressure_reference).
+template <int N>
+constexpr int kPressureNode = (N / 2) * (1 + (N + 1) + (N + 1) * (N + 1));
+
 // Global values one thread loads for phase A: IT nodes x (5 fields, phi,
 // with PERT the reference density and pressure, 9 metric terms when staged,
 // J).
-template <typename T, int N, class C, bool PERT = false>
+template <typename T, int N, class C, bool PERT = false, bool PSPLIT = false>
 struct NodeLoads {
     using S = Shape<N, C>;
     static constexpr int IT = S::kNodeIters;
-    T v[IT][PERT ? 8 : 6];
+    T v[IT][PSPLIT ? 9 : PERT ? 8 : 6];
     T m[C::kMetricInLds ? IT : 1][9];
     T J[IT];
     __device__ inline void issue(const T *__restrict__ q, const T *__restrict__ ref,
@@ -500,6 +528,10 @@ struct NodeLoads {
                 if constexpr (PERT) {
                     v[it][6] = ref[g];
                     v[it][7] = ref[fstride + g];
+                }
+                if constexpr (PSPLIT) {
+                    // the element's reference pressure P (pressure_reference)
+                    v[it][8] = ref[fstride + B.g0 + (t / S::Np) * S::Np + kPressureNode<N>];
                 }
                 if constexpr (C::kMetricInLds) {
 #pragma unroll
@@ -525,9 +557,13 @@ struct NodeLoads {
 // the same pressure law with the reference's share taken out before the
 // subtraction, so the small differences are formed without the large
 // reference values.
-template <typename T, bool PERT = false>
+//
+// With PSPLIT (perturbation variables in fp32) the node also gets
+// bd = b (p - P) for the split pressure (pressure_reference), with
+// p - P = (pbar - P) + (gamma-1)(...) formed without p itself.
+template <typename T, bool PERT = false, bool PSPLIT = false>
 __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rbar = T(0),
-                                          T pbar = T(0))
+                                          T pbar = T(0), T P = T(0))
 {
     using A = Arith<T>;
     const T gm1 = T(kGamma - 1.0);
@@ -545,6 +581,7 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
     const T p = PERT ? fma(gm1, dE, pbar) : gm1 * dE;
     V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
     V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
+    if constexpr (PSPLIT) V.bd = V.b * fma(gm1, dE, pbar - P);
     V.lrho = A::node_log(rho);
     V.lb = A::node_log(V.b);
     V.ph = T(0.25) * ph;                          // phi/4
@@ -553,8 +590,8 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
 }
 
 // Phase A compute: per-node primitives and logs into LDS; returns -1/J per node.
-template <typename T, int N, class C, bool PERT>
-__device__ inline void stage_nodes(const NodeLoads<T, N, C, PERT> &L, const Batch<N, C> &B,
+template <typename T, int N, class C, bool PERT, bool PSPLIT = false>
+__device__ inline void stage_nodes(const NodeLoads<T, N, C, PERT, PSPLIT> &L, const Batch<N, C> &B,
                                    T *lds, T (&mJ)[Shape<N, C>::kNodeIters])
 {
     using A = Arith<T>;
@@ -565,7 +602,11 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C, PERT> &L, const Batc
         if (t < B.nvalid) {
             const int st = Shape<N, C>::slot(t);
             NodeRegs<T> V;
-            if constexpr (PERT)
+            if constexpr (PSPLIT)
+                V = node_values<T, true, true>(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
+                                               L.v[it][4], L.v[it][5], L.v[it][6], L.v[it][7],
+                                               L.v[it][8]);
+            else if constexpr (PERT)
                 V = node_values<T, true>(L.v[it][0], L.v[it][1], L.v[it][2], L.v[it][3],
                                          L.v[it][4], L.v[it][5], L.v[it][6], L.v[it][7]);
             else
@@ -581,6 +622,7 @@ __device__ inline void stage_nodes(const NodeLoads<T, N, C, PERT> &L, const Batc
             lds[kPhi * SLOTS + st] = V.ph;
             lds[kW * SLOTS + st] = V.w;
             lds[kInvB * SLOTS + st] = V.ib;
+            if constexpr (PSPLIT) lds[Shape<N, C>::kBDelta * SLOTS + st] = V.bd;
             if constexpr (C::kMetricInLds) {
 #pragma unroll
                 for (int j = 0; j < 9; ++j) lds[(kJa + j) * SLOTS + st] = L.m[it][j];
@@ -632,8 +674,13 @@ struct FaceLoads {
             }
         }
     }
-    __device__ inline NodeRegs<T> partner(int end) const {
-        if constexpr (PERT)
+    // P: the own element's reference pressure (PSPLIT)
+    template <bool PSPLIT = false>
+    __device__ inline NodeRegs<T> partner(int end, T P = T(0)) const {
+        if constexpr (PSPLIT)
+            return node_values<T, true, true>(v[end][0], v[end][1], v[end][2], v[end][3],
+                                              v[end][4], v[end][5], v[end][6], v[end][7], P);
+        else if constexpr (PERT)
             return node_values<T, true>(v[end][0], v[end][1], v[end][2], v[end][3], v[end][4],
                                         v[end][5], v[end][6], v[end][7]);
         else
@@ -641,10 +688,10 @@ struct FaceLoads {
     }
 };
 
-template <typename T, int N, class C, bool PERT>
+template <typename T, int N, class C, bool PERT, bool PSPLIT = false>
 __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
                                     const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
-                                    const FaceLoads<T, PERT> &F, int64_t nelem,
+                                    const FaceLoads<T, PERT> &F, int64_t nelem, T P,
                                     T (&acc)[N + 1][5])
 {
     using A = Arith<T>;
@@ -659,6 +706,7 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
         const int a = end ? N : 0;
         NodeRegs<T> X;
         X.load_state(lds, SLOTS, L.nb + a * L.step);
+        if constexpr (PSPLIT) X.load_bd(lds, SLOTS, L.nb + a * L.step, Shape<N, C>::kBDelta);
         if constexpr (C::kMetricInLds) {
             X.load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
         } else {
@@ -673,14 +721,14 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
             Y.u2 = X.u2 - un2 * X.n2;
             Y.u3 = X.u3 - un2 * X.n3;
         } else if (nb >= 0 && nb < nelem) {
-            Y = F.partner(end);
+            Y = F.template partner<PSPLIT>(end, P);
             Y.n1 = X.n1; Y.n2 = X.n2; Y.n3 = X.n3;
         } else {
             Y.rho = T(__builtin_nan(""));  // invalid neighbour index: the result says so
         }
         const T coef = end ? T(kEnd) : T(-kEnd);
         T partner[5] = {T(0), T(0), T(0), T(0), T(0)};
-        pair_update(X, Y, &coef, &coef, acc[a], partner);
+        pair_update<T, false, PSPLIT>(X, Y, &coef, &coef, acc[a], partner, P);
     }
 }
 
@@ -710,18 +758,19 @@ __device__ inline bool line_in_series(const T *lds, const LineTask<N, C> &L)
 }
 
 // Phase B: every unordered pair of this thread's line.
-template <typename T, int N, class C, bool SERIES>
+template <typename T, int N, class C, bool SERIES, bool PSPLIT>
 __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
                                        const LineTask<N, C> &L,
                                        const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
-                                       T (&acc)[N + 1][5])
+                                       T (&acc)[N + 1][5], T P)
 {
-    constexpr int Nq = N + 1, SLOTS = Shape<N, C>::kSlots;
+    constexpr int Nq = N + 1, SLOTS = Shape<N, C>::kSlots, BD = Shape<N, C>::kBDelta;
     if constexpr (C::kCacheLine) {
         NodeRegs<T> V[Nq];
 #pragma unroll
         for (int a = 0; a < Nq; ++a) {
             V[a].load_state(lds, SLOTS, L.nb + a * L.step);
+            if constexpr (PSPLIT) V[a].load_bd(lds, SLOTS, L.nb + a * L.step, BD);
             if constexpr (C::kMetricInLds) {
                 V[a].load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
             } else {
@@ -732,7 +781,8 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
         for (int a = 0; a < Nq - 1; ++a)
 #pragma unroll
             for (int l = a + 1; l < Nq; ++l)
-                pair_update<T, SERIES>(V[a], V[l], D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+                pair_update<T, SERIES, PSPLIT>(V[a], V[l], D + a * Nq + l, D + l * Nq + a,
+                                               acc[a], acc[l], P);
         return;
     }
 #pragma unroll
@@ -742,6 +792,7 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
         asm volatile("" ::: "memory");
         NodeRegs<T> X;
         X.load_state(lds, SLOTS, L.nb + a * L.step);
+        if constexpr (PSPLIT) X.load_bd(lds, SLOTS, L.nb + a * L.step, BD);
         if constexpr (C::kMetricInLds) {
             X.load_metric(lds, SLOTS, L.nb + a * L.step, L.k);
         } else {
@@ -751,12 +802,14 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
         for (int l = a + 1; l < Nq; ++l) {
             NodeRegs<T> Y;
             Y.load_state(lds, SLOTS, L.nb + l * L.step);
+            if constexpr (PSPLIT) Y.load_bd(lds, SLOTS, L.nb + l * L.step, BD);
             if constexpr (C::kMetricInLds) {
                 Y.load_metric(lds, SLOTS, L.nb + l * L.step, L.k);
             } else {
                 Y.n1 = lm[l][0]; Y.n2 = lm[l][1]; Y.n3 = lm[l][2];
             }
-            pair_update<T, SERIES>(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l]);
+            pair_update<T, SERIES, PSPLIT>(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l],
+                                           P);
         }
     }
 }
@@ -765,15 +818,74 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
 // the wave is within the series threshold (smooth flow), the pairs skip the
 // log branch and the selects; otherwise each pair selects for itself.  Both
 // forms give the same values.
-template <typename T, int N, class C, bool SPLIT>
+template <typename T, int N, class C, bool SPLIT, bool PSPLIT = false>
 __device__ inline void line_pairs(const T *lds, const T *__restrict__ D, const LineTask<N, C> &L,
                                   const T (&lm)[C::kMetricInLds ? 1 : N + 1][3],
-                                  T (&acc)[N + 1][5])
+                                  T (&acc)[N + 1][5], T P = T(0))
 {
     if (SPLIT && __all(line_in_series<T, N, C>(lds, L)))
-        line_pairs_form<T, N, C, true>(lds, D, L, lm, acc);
+        line_pairs_form<T, N, C, true, PSPLIT>(lds, D, L, lm, acc, P);
     else
-        line_pairs_form<T, N, C, false>(lds, D, L, lm, acc);
+        line_pairs_form<T, N, C, false, PSPLIT>(lds, D, L, lm, acc, P);
+}
+
+// Split pressure (PSPLIT; the fp32 kernels on perturbation variables).
+// The momentum flux of a pair carries the pressure mean p^ = {{rho}}/(2{{b}})
+// times the pair's metric c = Ja^k(a) + Ja^k(l); for a state near
+// hydrostatic balance p^ is O(p) while the line's net momentum flux is far
+// smaller, so rounding p^ c to fp32 in every pair leaves noise of
+// eps * p * |Ja| * sum|D| in the momentum.  For any P fixed per element,
+//     p^ = P + (b_a (p_a - P) + b_l (p_l - P)) / (b_a + b_l)
+// exactly, with b = rho/(2p).  The pairs and the face ends take the second
+// part, formed from the staged b (p - P) (small near balance, so its
+// rounding is small), and this function adds the first part once per line
+// node: P times the sum over the line's pairs of D_al c_m and over its face
+// ends of +-N(N+1)/4 * 2 Ja^k_m(a), a sum of metric and D values only that
+// is formed in fp64, where the fp32 products are exact and the face parts
+// cancel the volume's end-node parts without rounding.  P is the element's
+// reference pressure at its node (N/2, N/2, N/2), the same for the element's
+// nodes, lines and face partners.
+template <typename T, int N, class C>
+__device__ inline void pressure_reference(const T *lds, const T *__restrict__ D,
+                                          const LineTask<N, C> &L,
+                                          const T (&lm)[C::kMetricInLds ? 1 : N + 1][3], T P,
+                                          T (&acc)[N + 1][5])
+{
+    constexpr int Nq = N + 1, SLOTS = Shape<N, C>::kSlots;
+    constexpr double kEnd2 = N * (N + 1) / 2.0;  // 2 x the face coefficient N(N+1)/4
+    // P Ja^k_m(l) in fp64 (exact: a product of two fp32 values)
+    double pj[Nq][3];
+    const double Pd = (double)P;
+#pragma unroll
+    for (int l = 0; l < Nq; ++l) {
+        T n[3];
+        if constexpr (C::kMetricInLds) {
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+                n[m] = lds[(kJa + 3 * L.k + m) * SLOTS + L.nb + l * L.step];
+        } else {
+#pragma unroll
+            for (int m = 0; m < 3; ++m) n[m] = lm[l][m];
+        }
+#pragma unroll
+        for (int m = 0; m < 3; ++m) pj[l][m] = Pd * (double)n[m];
+    }
+#pragma unroll
+    for (int a = 0; a < Nq; ++a) {
+        // P sum_l D_al (Ja(a) + Ja(l)) + face part = P Ja(a) rs + sum_l D_al P Ja(l)
+        double rs = (a == N) ? kEnd2 : (a == 0) ? -kEnd2 : 0.0;
+        double g[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+        for (int l = 0; l < Nq; ++l) {
+            if (l == a) continue;
+            const double d = (double)D[a * Nq + l];
+            rs += d;
+#pragma unroll
+            for (int m = 0; m < 3; ++m) g[m] = fma(d, pj[l][m], g[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[a][1 + m] += (T)fma(pj[a][m], rs, g[m]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,7 +1238,10 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     static_assert(SURF || !(STAGE || PERT), "stages and perturbation variables need the whole rhs");
     using S = Shape<N, C>;
     constexpr int Nq = N + 1;
-    __shared__ T lds[S::kLdsValues];
+    // fp32 on perturbation variables splits the pressure (pressure_reference)
+    constexpr bool PSPLIT = PERT && sizeof(T) == 4;
+    static_assert(!PSPLIT || C::kLanes == 1, "the split pressure takes one lane per line");
+    __shared__ T lds[S::template kLdsValues<PSPLIT>];
     const int64_t fstride = nelem * S::Np;
     // the whole right-hand side walks the batches in XCD-contiguous order
     const int64_t batch = SURF ? xcd_batch(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
@@ -1187,8 +1302,12 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     if constexpr (SURF) {
         if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
     }
-    NodeLoads<T, N, C, PERT> ld;
+    NodeLoads<T, N, C, PERT, PSPLIT> ld;
     ld.issue(q, ref, phi, geom, fstride, B);
+    T P = T(0);  // the element's reference pressure (PSPLIT)
+    if constexpr (PSPLIT) {
+        if (active) P = ref[fstride + B.g0 + L.eb * S::Np + kPressureNode<N>];
+    }
     T lm[C::kMetricInLds ? 1 : Nq][3];
     if constexpr (!C::kMetricInLds) {
         if (active) {
@@ -1204,7 +1323,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
                                                      L.first_in_element(), L.node_step());
     }
     T mJ[S::kNodeIters];
-    stage_nodes<T, N, C, PERT>(ld, B, lds, mJ);
+    stage_nodes<T, N, C, PERT, PSPLIT>(ld, B, lds, mJ);
     __syncthreads();
 
     // phase B
@@ -1215,10 +1334,13 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         for (int f = 0; f < 5; ++f) acc[a][f] = T(0);
     // the face partners first: their loaded states die before the pair loop
     if constexpr (SURF) {
-        if (active) surface_ends<T, N, C, PERT>(lds, L, lm, face, nelem, acc);
+        if (active) surface_ends<T, N, C, PERT, PSPLIT>(lds, L, lm, face, nelem, P, acc);
     }
     constexpr bool kSplit = SURF ? C::kSeriesFormSurf : C::kSeriesForm;
-    if (active) line_pairs<T, N, C, kSplit>(lds, D, L, lm, acc);
+    if (active) line_pairs<T, N, C, kSplit, PSPLIT>(lds, D, L, lm, acc, P);
+    if constexpr (PSPLIT) {
+        if (active) pressure_reference<T, N, C>(lds, D, L, lm, P, acc);
+    }
     __syncthreads();  // node values are dead from here on: LDS becomes the partials
 
     // phases C, D

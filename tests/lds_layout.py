@@ -58,6 +58,7 @@ class Shape:
     N: int
     cfg: dict
     dtype: str = "double"
+    split: bool = False   # the fp32 perturbation kernels stage b (p - P) too
 
     def __post_init__(self):
         c = self.cfg
@@ -77,7 +78,9 @@ class Shape:
         staged = STAGED_WITH_METRIC if c["metric_lds"] else STAGED_NO_METRIC
         partials = PARTIALS_FIN if c["fin"] else PARTIALS
         self.region = max(staged, partials) + (1 if c["fin"] else 0)
-        self.lds_bytes = self.region * self.slots * (8 if self.dtype == "double" else 4)
+        # the extra value sits in the shared region when the partials leave it free
+        self.values = self.region + (1 if self.split and staged >= partials else 0)
+        self.lds_bytes = self.values * self.slots * (8 if self.dtype == "double" else 4)
 
     def slot(self, t: int) -> int:
         """LDS slot of node t of the workgroup (t = e Np + x + Nq y + Nq^2 z)."""

@@ -241,8 +241,12 @@ def test_fp32_noise_full_against_perturbation_variables():
     whole right-hand side of the near-balanced bubble against the oracle on
     the same represented state, error over max |rhs| itself, with full state
     variables and with perturbation variables about the hydrostatic base.
-    Both must meet the parity bar (over the summed magnitudes); the printed
-    figures are what the comparison shows."""
+    Both must meet the parity bar (over the summed magnitudes).  With full
+    state variables the momentum error exceeds the momentum rhs itself (the
+    pressure is rounded at O(p) in every pair); the perturbation kernels form
+    the pressure relative to each element's reference pressure, and their
+    horizontal-momentum error must stay below half the rhs and at least 20x
+    below the full-state error (measured: 0.06 against 7.4)."""
     wl32 = I.make("bubble_f32")
     got_full = gpu_rhs(wl32.q, wl32.phi, wl32.geom, wl32.D, wl32.nbr)
     want_full, mag_full = oracle.rhs(wl32.q, wl32.phi, wl32.geom, wl32.D, wl32.nbr, wl32.N,
@@ -257,6 +261,9 @@ def test_fp32_noise_full_against_perturbation_variables():
     print(f"[pert] bubble fp32 full state:    err/max|rhs| {['%.2e' % e for e in r_full]}", flush=True)
     print(f"[pert] bubble fp32 perturbations: err/max|rhs| {['%.2e' % e for e in r_pert]}", flush=True)
     assert max(m_full) <= TOL[np.float32] and max(m_pert) <= TOL[np.float32]
+    for f in (1, 2):
+        assert r_pert[f] <= 0.5, (f, r_pert)
+        assert r_pert[f] * 20 <= r_full[f], (f, r_pert, r_full)
 
 
 # --- conservation integrals ------------------------------------------------------------
