@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 HEADLINE = "bubble"
 METRIC = "volume-RHS DOF-updates/s and FP64 GFLOP/s (% of FP64 vector peak), N=4, 1 GPU"
-SOURCES = ("entropy_stable_dg_amd/csrc/volume_kernel.hpp", "entropy_stable_dg_amd/csrc/esdg_api.hip")
+SOURCES = ("entropy_stable_dg_amd/csrc/volume_kernel.hpp", "entropy_stable_dg_amd/csrc/esdg_api.hip",
+           "entropy_stable_dg_amd/csrc/launch_table.hpp")
 
 
 def log(msg: str) -> None:

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libesdg.so")
 SOURCES = [os.path.join(CSRC, "esdg_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"), os.path.join(INCLUDE, "esdg.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"), os.path.join(CSRC, "launch_table.hpp"),
+                     os.path.join(INCLUDE, "esdg.h")]
 # HBM streaming probes (measurement only), a library of their own
 PROBE_LIB = os.path.join(HERE, "libesdg_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
@@ -60,6 +61,7 @@ def build(verbose: bool = False) -> str:
 def is_stale() -> bool:
     """True when the library is missing or older than one of its sources."""
     probe_deps = PROBE_SOURCES + [os.path.join(CSRC, "volume_kernel.hpp"),
+                                  os.path.join(CSRC, "launch_table.hpp"),
                                   os.path.join(INCLUDE, "esdg_probe.h")]
     for lib, deps in ((LIB, DEPENDS), (PROBE_LIB, probe_deps), (ABLATION_LIB, ABLATION_DEPENDS)):
         if not os.path.exists(lib):

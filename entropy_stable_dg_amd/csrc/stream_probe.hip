@@ -9,6 +9,7 @@
 
 #include "esdg_probe.h"
 #include "volume_kernel.hpp"
+#include "launch_table.hpp"
 
 namespace {
 
@@ -93,9 +94,104 @@ int check(const void *src, const void *dst, int64_t n, int64_t arrays)
     return 0;
 }
 
+// Phase timeline of the library's volume kernel (or whole right-hand side
+// when nbr is given): the same kernel instance with WallMarks.
+template <typename T, int N>
+int64_t timeline_workgroups(int64_t nelem)
+{
+    using C = typename esdg::Launch<T, N>::C;
+    return (nelem + C::EPB - 1) / C::EPB;
+}
+
+template <typename T>
+int64_t workgroups_of(int N, int64_t nelem)
+{
+    switch (N) {
+        case 1: return timeline_workgroups<T, 1>(nelem);
+        case 2: return timeline_workgroups<T, 2>(nelem);
+        case 3: return timeline_workgroups<T, 3>(nelem);
+        case 4: return timeline_workgroups<T, 4>(nelem);
+        case 5: return timeline_workgroups<T, 5>(nelem);
+        case 6: return timeline_workgroups<T, 6>(nelem);
+        case 7: return timeline_workgroups<T, 7>(nelem);
+        case 8: return timeline_workgroups<T, 8>(nelem);
+    }
+    return -3;
+}
+
+template <typename T, int N>
+int timeline_launch(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr,
+                    int64_t nelem, T *rhs, uint64_t *marks, hipStream_t stream)
+{
+    using C = typename esdg::Launch<T, N>::C;
+    const int64_t blocks = timeline_workgroups<T, N>(nelem);
+    const esdg::Rotation<T> rot{T(0), T(0), T(0), false};
+    const esdg::Sink<T, false> sink{rhs, nullptr, T(0), T(0), T(0)};
+    const esdg::WallMarks wm{(unsigned long long *)marks};
+    if (nbr)
+        hipLaunchKernelGGL((esdg::volume_rhs_kernel<T, N, C, true, false, false, esdg::WallMarks>),
+                           dim3((unsigned)blocks), dim3(C::NT), 0, stream, q, (const T *)nullptr,
+                           phi, geom, D, nbr, rot, nelem, sink, wm);
+    else
+        hipLaunchKernelGGL((esdg::volume_rhs_kernel<T, N, C, false, false, false, esdg::WallMarks>),
+                           dim3((unsigned)blocks), dim3(C::NT), 0, stream, q, (const T *)nullptr,
+                           phi, geom, D, (const int32_t *)nullptr, rot, nelem, sink, wm);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <typename T>
+int timeline(const T *q, const T *phi, const T *geom, const T *D, const int32_t *nbr, int N,
+             int64_t nelem, T *rhs, uint64_t *marks, hipStream_t stream)
+{
+    if (N < 1 || N > 8 || nelem < 0) return -3;
+    const int64_t Np = (int64_t)(N + 1) * (N + 1) * (N + 1);
+    if (nelem > INT64_MAX / (10 * Np * (int64_t)sizeof(T)) || workgroups_of<T>(N, nelem) > INT32_MAX)
+        return -3;
+    if (nelem == 0) return 0;
+    if (!q || !phi || !geom || !D || !rhs || !marks) return -1;
+    switch (N) {
+        case 1: return timeline_launch<T, 1>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 2: return timeline_launch<T, 2>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 3: return timeline_launch<T, 3>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 4: return timeline_launch<T, 4>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 5: return timeline_launch<T, 5>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 6: return timeline_launch<T, 6>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 7: return timeline_launch<T, 7>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+        case 8: return timeline_launch<T, 8>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
+    }
+    return -3;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t esdg_probe_timeline_workgroups(int N, int64_t nelem, int fp64)
+{
+    if (N < 1 || N > 8 || nelem < 0) return -3;
+    return fp64 ? workgroups_of<double>(N, nelem) : workgroups_of<float>(N, nelem);
+}
+
+int esdg_probe_timeline_f64(const double *q, const double *phi, const double *geom,
+                            const double *D, const int32_t *nbr, int N, int64_t nelem,
+                            double *rhs, uint64_t *marks, hipStream_t stream)
+{
+    return timeline<double>(q, phi, geom, D, nbr, N, nelem, rhs, marks, stream);
+}
+
+int esdg_probe_timeline_f32(const float *q, const float *phi, const float *geom, const float *D,
+                            const int32_t *nbr, int N, int64_t nelem, float *rhs,
+                            uint64_t *marks, hipStream_t stream)
+{
+    return timeline<float>(q, phi, geom, D, nbr, N, nelem, rhs, marks, stream);
+}
+
+int esdg_probe_wall_clock_khz(void)
+{
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, 0) != hipSuccess) return -4;
+    return khz;
+}
 
 int esdg_probe_stream81_f64(const double *src, double *dst, int64_t n, hipStream_t stream)
 {

@@ -1221,19 +1221,47 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
     }
 }
 
+// Phase marks for the measurement probes: NoMarks (the library's kernels)
+// compiles to nothing; WallMarks has lane 0 of each workgroup write the wall
+// clock on entry (0), after phase A's barrier (1), after phase B's barrier
+// (2) and after its last store is issued (3), then the hardware id of its
+// compute unit (4) and its batch (5), to out[blockIdx.x * kMarkValues + i].
+constexpr int kMarkValues = 6;
+
+struct NoMarks {
+    static constexpr bool on = false;
+    __device__ inline void at(int) const {}
+    __device__ inline void where(int64_t) const {}
+};
+
+struct WallMarks {
+    static constexpr bool on = true;
+    unsigned long long *out;
+    __device__ inline void at(int i) const {
+        if (threadIdx.x == 0) out[(int64_t)blockIdx.x * kMarkValues + i] = (unsigned long long)wall_clock64();
+    }
+    __device__ inline void where(int64_t batch) const {
+        if (threadIdx.x == 0) {
+            out[(int64_t)blockIdx.x * kMarkValues + 4] = __smid();
+            out[(int64_t)blockIdx.x * kMarkValues + 5] = (unsigned long long)batch;
+        }
+    }
+};
+
 // One workgroup per batch of EPB elements.  SURF adds the entropy-conservative
 // surface term (face neighbours from nbr), giving the whole right-hand side;
 // rot.on adds the Coriolis source.  STAGE fuses a Runge-Kutta stage into the
 // store (Sink); PERT reads the state as perturbation variables about the
 // reference ref = (rbar, pbar) (node_values).
-template <typename T, int N, class C, bool SURF = false, bool STAGE = false, bool PERT = false>
+template <typename T, int N, class C, bool SURF = false, bool STAGE = false, bool PERT = false,
+          class Marks = NoMarks>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, C::NT)))
 __attribute__((amdgpu_waves_per_eu(SURF ? (C::WAVES_SURF > 0 ? C::WAVES_SURF : 1)
                                          : (C::WAVES > 0 ? C::WAVES : 1))))
 volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *__restrict__ phi,
                   const T *__restrict__ geom, const T *__restrict__ D,
                   const int32_t *__restrict__ nbr, Rotation<T> rot, int64_t nelem,
-                  Sink<T, STAGE> sink)
+                  Sink<T, STAGE> sink, Marks marks = Marks())
 {
     static_assert(SURF || !(STAGE || PERT), "stages and perturbation variables need the whole rhs");
     using S = Shape<N, C>;
@@ -1249,6 +1277,8 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     const LineTask<N, C> L;
     const bool active = L.active(B.nvalid);
     if constexpr (!SURF) rot.on = false;  // the volume term alone has no source
+    marks.at(0);
+    marks.where(batch);
 
     // phase A: issue every global load first
     if constexpr (C::kLanes == 2) {
@@ -1274,6 +1304,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         T mJ[S::kNodeIters];
         stage_nodes<T, N, C, PERT>(ld, B, lds, mJ);
         __syncthreads();
+        marks.at(1);
 
         // phase B
         T acc[H][5];
@@ -1287,6 +1318,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         constexpr bool kSplit = SURF ? C::kSeriesFormSurf : C::kSeriesForm;
         if (active) line_pairs_x2<T, N, C, kSplit>(lds, D, L, lm, acc);
         __syncthreads();
+        marks.at(2);
 
         // phases C, D
         write_partials_x2<T, N, C>(lds, L, active, acc);
@@ -1295,6 +1327,10 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
             finish_line_x2<T, N, C, STAGE>(lds, L, active, B, fstride, acc, q, rot, sink);
         } else {
             store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
+        }
+        if constexpr (Marks::on) {
+            __syncthreads();
+            marks.at(3);
         }
         return;
     } else {
@@ -1325,6 +1361,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     T mJ[S::kNodeIters];
     stage_nodes<T, N, C, PERT, PSPLIT>(ld, B, lds, mJ);
     __syncthreads();
+    marks.at(1);
 
     // phase B
     T acc[Nq][5];
@@ -1342,6 +1379,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         if (active) pressure_reference<T, N, C>(lds, D, L, lm, P, acc);
     }
     __syncthreads();  // node values are dead from here on: LDS becomes the partials
+    marks.at(2);
 
     // phases C, D
     write_partials<T, N, C>(lds, L, active, acc);
@@ -1350,6 +1388,10 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         finish_line<T, N, C, STAGE>(lds, L, active, B, fstride, acc, q, rot, sink);
     } else {
         store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
+    }
+    if constexpr (Marks::on) {
+        __syncthreads();
+        marks.at(3);
     }
     }
 }

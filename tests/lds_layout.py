@@ -1,7 +1,7 @@
 """Host-side model of the kernel's launch shapes and LDS layout, for checking
 a launch table on the CPU before it runs on a GPU.
 
-It reads the `Launch<T, N>` table of csrc/esdg_api.hip and derives, for each
+It reads the `Launch<T, N>` table of csrc/launch_table.hpp and derives, for each
 shape, what the kernel derives from its `LaunchCfg`: the LDS slot of every
 node of a workgroup (node grid x + R y + P z + E e with the row, plane and
 element pads), the line task of every thread (element-major, direction-major,
@@ -21,7 +21,7 @@ import re
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "esdg_api.hip")
+API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "launch_table.hpp")
 
 # LaunchCfg<EPB, NT, WAVES, METRIC_LDS, CACHE, KMAJOR, FIN, SERIES, SERIES_SURF,
 #           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES> and its defaults

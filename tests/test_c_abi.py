@@ -35,6 +35,15 @@ int main(void)
     if (esdg_ablation_volume_rhs_f64(ESDG_ABL_COUNT, p, p, p, p, 4, 1, r, 0) != ESDG_ERR_VARIANT) fails++;
     if (strcmp(esdg_ablation_name(ESDG_ABL_BASELINE), "baseline") != 0) fails++;
     if (esdg_probe_copy_f64(p, r, -1, 0) != -3) fails++;
+    /* the timeline's workgroup count follows the launch table: 3 elements per
+       workgroup at N = 4, one at N = 7 */
+    if (esdg_probe_timeline_workgroups(4, 4096, 1) != 1366) fails++;
+    if (esdg_probe_timeline_workgroups(4, 4096, 0) != 1366) fails++;
+    if (esdg_probe_timeline_workgroups(7, 13824, 1) != 13824) fails++;
+    if (esdg_probe_timeline_workgroups(9, 10, 1) != -3) fails++;
+    if (esdg_probe_timeline_f64(p, p, p, p, 0, 9, 1, r, (uint64_t *)r, 0) != -3) fails++;
+    if (esdg_probe_timeline_f64(p, p, p, p, 0, 4, 1, r, (uint64_t *)0, 0) != -1) fails++;
+    if (esdg_probe_timeline_f32(0, 0, 0, 0, 0, 4, 0, 0, 0, 0) != 0) fails++;
     printf("fails=%d\n", fails);
     return fails;
 }

@@ -2,7 +2,7 @@
 of every phase, replayed on the CPU for every compiled order, stays inside the
 buffers it touches, and each (direction, node) partial-sum slot in LDS is
 written by exactly one line thread.  Mirrors entropy_stable_dg_amd/csrc
-(volume_kernel.hpp and the launch table in esdg_api.hip)."""
+(volume_kernel.hpp and the launch table in launch_table.hpp)."""
 import re
 
 import numpy as np
@@ -11,7 +11,7 @@ import pytest
 import os
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-API = os.path.join(ROOT, "entropy_stable_dg_amd", "csrc", "esdg_api.hip")
+API = os.path.join(ROOT, "entropy_stable_dg_amd", "csrc", "launch_table.hpp")
 KERNEL = os.path.join(ROOT, "entropy_stable_dg_amd", "csrc", "volume_kernel.hpp")
 
 NODE_VALUES = 19     # staged values per node (10 state values + 9 metric terms)
@@ -19,7 +19,7 @@ PARTIAL_VALUES = 15  # 3 directions x 5 fields
 
 
 def launch_table():
-    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major, finish_in_line)} from esdg_api.hip."""
+    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major, finish_in_line)} from launch_table.hpp."""
     text = open(API).read()
     rows = re.findall(r"struct Launch<(double|float), (\d+)>\s*\{\s*using C = LaunchCfg<([^>]*)>;", text)
     table = {}
