@@ -149,6 +149,10 @@ int timeline(const T *q, const T *phi, const T *geom, const T *D, const int32_t 
         return -3;
     if (nelem == 0) return 0;
     if (!q || !phi || !geom || !D || !rhs || !marks) return -1;
+    // slot 3 of every workgroup is raised by each of its waves: start at zero
+    if (hipMemsetAsync(marks, 0, (size_t)workgroups_of<T>(N, nelem) * esdg::kMarkValues * 8,
+                       stream) != hipSuccess)
+        return -4;
     switch (N) {
         case 1: return timeline_launch<T, 1>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);
         case 2: return timeline_launch<T, 2>(q, phi, geom, D, nbr, nelem, rhs, marks, stream);

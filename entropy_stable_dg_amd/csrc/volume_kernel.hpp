@@ -1224,14 +1224,18 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
 // Phase marks for the measurement probes: NoMarks (the library's kernels)
 // compiles to nothing; WallMarks has lane 0 of each workgroup write the wall
 // clock on entry (0), after phase A's barrier (1), after phase B's barrier
-// (2) and after its last store is issued (3), then the hardware id of its
-// compute unit (4) and its batch (5), to out[blockIdx.x * kMarkValues + i].
+// (2), the hardware id of its compute unit (4) and its batch (5), and lane 0
+// of every wave raise slot 3 to the clock when the wave has issued its last
+// store (no barrier added: waves that finish early leave early, as in the
+// library's kernels), all to out[blockIdx.x * kMarkValues + i]; slot 3 must
+// start at zero.
 constexpr int kMarkValues = 6;
 
 struct NoMarks {
     static constexpr bool on = false;
     __device__ inline void at(int) const {}
     __device__ inline void where(int64_t) const {}
+    __device__ inline void wave_end() const {}
 };
 
 struct WallMarks {
@@ -1245,6 +1249,11 @@ struct WallMarks {
             out[(int64_t)blockIdx.x * kMarkValues + 4] = __smid();
             out[(int64_t)blockIdx.x * kMarkValues + 5] = (unsigned long long)batch;
         }
+    }
+    __device__ inline void wave_end() const {
+        if ((threadIdx.x & 63) == 0)
+            atomicMax(out + (int64_t)blockIdx.x * kMarkValues + 3,
+                      (unsigned long long)wall_clock64());
     }
 };
 
@@ -1328,10 +1337,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         } else {
             store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
         }
-        if constexpr (Marks::on) {
-            __syncthreads();
-            marks.at(3);
-        }
+        marks.wave_end();
         return;
     } else {
     FaceLoads<T, PERT> face;
@@ -1389,10 +1395,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     } else {
         store_rhs<T, N, C, STAGE>(lds, B, fstride, mJ, q, rot, sink);
     }
-    if constexpr (Marks::on) {
-        __syncthreads();
-        marks.at(3);
-    }
+    marks.wave_end();
     }
 }
 

@@ -52,8 +52,10 @@ int esdg_probe_copy_f64(const double *src, double *dst, int64_t n, hipStream_t s
  * kernel, launch shape and result, with lane 0 of every workgroup writing
  * marks[w * 6 + i] (uint64) for workgroup w: the device wall clock on entry
  * (i = 0), once its nodes are staged in LDS (1), once its line pairs are
- * done (2) and once its stores are issued (3); the hardware id of its compute
- * unit (4) and the batch of elements it took (5).  Arguments and layouts as
+ * done (2) and once its last wave has issued its stores (3, the latest of
+ * its waves' clocks; no barrier is added for it); the hardware id of its
+ * compute unit (4) and the batch of elements it took (5).  The call clears
+ * marks on the stream before the launch.  Arguments and layouts as
  * for esdg_volume_rhs_* / esdg_rhs_*; marks holds at least
  * 6 * esdg_probe_timeline_workgroups(N, nelem, fp64) values.  Inputs are
  * not checked for aliasing.  Returns 0, -1 NULL pointer, -3 N outside 1..8
