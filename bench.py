@@ -634,6 +634,8 @@ def main() -> int:
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the optimisation-ladder timing (N=4, 262,144 elements)")
     ap.add_argument("--ablation-steps", type=int, default=10)
+    ap.add_argument("--no-timeline", action="store_true",
+                    help="skip the phase timeline of the headline kernel (libesdg_probe)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the all-orders roofline sweep (N = 1..8, L = 3..6, fp64 and fp32); "
                          "prints its own JSON line")
@@ -745,6 +747,24 @@ def main() -> int:
 
     roofline, binding = roofline_of(achieved_gbs, gflops, stream_gbs, traffic)
 
+    # where the headline launch's time goes: phase marks of the same kernel
+    # (libesdg_probe), the launch with the median span of five
+    timeline = None
+    if not args.no_timeline:
+        _, runs = probe.timeline_runs(HEADLINE, runs=5, rotate_bytes=args.rotate_mb * 1e6)
+        ph = runs[len(runs) // 2]
+        timeline = {k: ph[k] for k in ("workgroups", "compute_units", "first_round", "span_us",
+                                       "first", "later", "first_round_staged_us",
+                                       "later_starts_us", "drain_us") if k in ph}
+        timeline["spans_us"] = [r["span_us"] for r in runs]
+        log(f"phase timeline: span {ph['span_us']:.2f} us; first round loads {ph['first']['load_stage_us']:.2f} us "
+            f"(median), pairs {ph['first']['pairs_us']:.2f} us; drain {ph['drain_us']:.2f} us")
+        if binding.startswith("neither"):
+            binding += (f"; phase timeline of the same kernel: the first round's {ph['first_round']} "
+                        f"workgroups load and stage for a median {ph['first']['load_stage_us']:.1f} us "
+                        f"before their pairs, and {ph['drain_us']:.1f} us of pairs and stores remain "
+                        f"after the last workgroup's loads")
+
     cpu = None
     cpu1 = None
     if not args.no_cpu_baseline:
@@ -781,6 +801,7 @@ def main() -> int:
                                           if counted_flops else None),
         "hbm_gbs_counted": traffic / t_cold / 1e9 if traffic else None,
         "binding_roof": binding,
+        "phase_timeline": timeline,
         "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
         "hot_ms_per_step": t_hot * 1e3,
         "hot_dof_per_s": info["dof"] / t_hot,

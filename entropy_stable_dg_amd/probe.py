@@ -159,6 +159,8 @@ def timeline_phases(marks, clock_hz: float, bins: int = 24) -> dict:
                         "pairs_us": float(np.median(d[:, 2] - d[:, 1])),
                         "store_us": float(np.median(d[:, 3] - d[:, 2]))}
     out["first_round_staged_us"] = [float(x) for x in np.percentile(t[first, 1], [10, 50, 90])]
+    # after the last workgroup's nodes are staged only pairs and stores remain
+    out["drain_us"] = span - float(t[:, 1].max())
     out["later_starts_us"] = ([float(x) for x in np.percentile(t[~first, 0], [0, 50, 100])]
                               if (~first).any() else [])
     rows = []
@@ -170,11 +172,11 @@ def timeline_phases(marks, clock_hz: float, bins: int = 24) -> dict:
     return out
 
 
-def timeline_report(name: str, whole: bool = False, runs: int = 5, rotate_bytes: float = 512e6) -> str:
-    """Markdown summary of the phase timeline of the library's kernel on a
-    named workload: buffers rotated over more than the Infinity Cache as the
-    benchmark does, a pre-roll of library launches, then `runs` timed
-    launches with marks; the run with the median span is tabulated."""
+def timeline_runs(name: str, whole: bool = False, runs: int = 5, rotate_bytes: float = 512e6):
+    """Phase summaries (timeline_phases) of `runs` launches of the library's
+    kernel with marks on a named workload, after buffers rotated over more
+    than the Infinity Cache and a pre-roll of library launches, as the
+    benchmark times them.  Returns (workload, summaries sorted by span)."""
     import math
     import time
 
@@ -212,8 +214,19 @@ def timeline_report(name: str, whole: bool = False, runs: int = 5, rotate_bytes:
         torch.cuda.synchronize()
         phases.append(timeline_phases(marks.cpu().numpy(), clock))
         i += 2
-    order = sorted(range(runs), key=lambda k: phases[k]["span_us"])
-    ph = phases[order[runs // 2]]
+    del sets, outs
+    torch.cuda.empty_cache()
+    return wl, sorted(phases, key=lambda ph: ph["span_us"])
+
+
+def timeline_report(name: str, whole: bool = False, runs: int = 5) -> str:
+    """Markdown summary of timeline_runs(): the launch with the median span
+    is tabulated."""
+    import numpy as np
+
+    wl, phases = timeline_runs(name, whole, runs)
+    order = list(range(runs))
+    ph = phases[runs // 2]
     dt = "fp64" if wl.q.dtype == np.float64 else "fp32"
     lines = [f"Workload `{name}` ({'whole right-hand side' if whole else 'volume term'}, {dt}, "
              f"N={wl.N}, {wl.nelem} elements): {ph['workgroups']} workgroups on "
@@ -232,8 +245,10 @@ def timeline_report(name: str, whole: bool = False, runs: int = 5, rotate_bytes:
     lines += ["", f"Medians in us.  First-round nodes staged at {p10:.2f} / {p50:.2f} / {p90:.2f} us "
               "(10th / 50th / 90th percentile of its workgroups)"
               + (f"; later workgroups start from {ph['later_starts_us'][0]:.2f} us, half by "
-                 f"{ph['later_starts_us'][1]:.2f} us, the last at {ph['later_starts_us'][2]:.2f} us."
-                 if ph["later_starts_us"] else "."),
+                 f"{ph['later_starts_us'][1]:.2f} us, the last at {ph['later_starts_us'][2]:.2f} us"
+                 if ph["later_starts_us"] else "")
+              + f".  After the last workgroup's nodes are staged, {ph['drain_us']:.2f} us of "
+                "pairs and stores remain.",
               "", "Workgroups in each phase over the launch:", "",
               "| t (us) | loading + staging | line pairs | partials + store |", "|---|---|---|---|"]
     for x, a, b, c in ph["occupancy"]:

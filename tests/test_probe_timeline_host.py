@@ -22,6 +22,8 @@ def test_timeline_phases_of_a_two_round_schedule():
     assert abs(ph["later"]["load_stage_us"] - 2) < 1e-9
     assert abs(ph["first"]["pairs_us"] - 3) < 1e-9 and abs(ph["later"]["store_us"] - 1) < 1e-9
     assert abs(ph["later_starts_us"][0] - 9) < 1e-9
+    # the last nodes are staged at 9.1 + 2 us; the span ends at 15.1 us
+    assert abs(ph["drain_us"] - (15.1 - 11.1)) < 1e-9
     occ = {round(x, 6): (a, b, c) for x, a, b, c in ph["occupancy"]}
     # at 6.04 us both first workgroups compute; at 10.07 both later ones load
     x = [k for k in occ if 6.0 < k < 6.6][0]
