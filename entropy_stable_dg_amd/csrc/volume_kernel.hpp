@@ -560,8 +560,10 @@ struct NodeLoads {
 //
 // With PSPLIT (perturbation variables in fp32) the node also gets
 // bd = b (p - P) for the split pressure (pressure_reference), with
-// p - P = (pbar - P) + (gamma-1)(...) formed without p itself.
-template <typename T, bool PERT = false, bool PSPLIT = false>
+// p - P = (pbar - P) + (gamma-1)(...) formed without p itself.  Without
+// LOGS the two logs are left out (a face partner whose pair takes the
+// series form of both log means does not need them).
+template <typename T, bool PERT = false, bool PSPLIT = false, bool LOGS = true>
 __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rbar = T(0),
                                           T pbar = T(0), T P = T(0))
 {
@@ -582,8 +584,10 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
     V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
     V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
     if constexpr (PSPLIT) V.bd = V.b * fma(gm1, dE, pbar - P);
-    V.lrho = A::node_log(rho);
-    V.lb = A::node_log(V.b);
+    if constexpr (LOGS) {
+        V.lrho = A::node_log(rho);
+        V.lb = A::node_log(V.b);
+    }
     V.ph = T(0.25) * ph;                          // phi/4
     V.w = fma(T(0.5), ph, -usq4);                 // w/2 = (phi - |u|^2/2)/2
     return V;
@@ -674,17 +678,19 @@ struct FaceLoads {
             }
         }
     }
-    // P: the own element's reference pressure (PSPLIT)
-    template <bool PSPLIT = false>
+    // P: the own element's reference pressure (PSPLIT); LOGS as node_values
+    template <bool PSPLIT = false, bool LOGS = true>
     __device__ inline NodeRegs<T> partner(int end, T P = T(0)) const {
         if constexpr (PSPLIT)
-            return node_values<T, true, true>(v[end][0], v[end][1], v[end][2], v[end][3],
-                                              v[end][4], v[end][5], v[end][6], v[end][7], P);
+            return node_values<T, true, true, LOGS>(v[end][0], v[end][1], v[end][2], v[end][3],
+                                                    v[end][4], v[end][5], v[end][6], v[end][7],
+                                                    P);
         else if constexpr (PERT)
-            return node_values<T, true>(v[end][0], v[end][1], v[end][2], v[end][3], v[end][4],
-                                        v[end][5], v[end][6], v[end][7]);
+            return node_values<T, true, false, LOGS>(v[end][0], v[end][1], v[end][2], v[end][3],
+                                                     v[end][4], v[end][5], v[end][6], v[end][7]);
         else
-            return node_values(v[end][0], v[end][1], v[end][2], v[end][3], v[end][4], v[end][5]);
+            return node_values<T, false, false, LOGS>(v[end][0], v[end][1], v[end][2],
+                                                      v[end][3], v[end][4], v[end][5]);
     }
 };
 
@@ -700,7 +706,11 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
     // with the LGL end weight w_end = 2/(N(N+1)); pair_update contracts with
     // Ja^k(own) + Ja^k(partner) = 2 Ja^k(own), so the coefficient is
     // +-1/(2 w_end) = +-N(N+1)/4.
+    // A partner's logs are formed only when some lane of the wave has a face
+    // pair outside the log means' series threshold (one wave vote per end,
+    // the general form's own test): the series form gives the same values.
     constexpr double kEnd = N * (N + 1) / 4.0;
+    const T eps = T(A::kSeries);
 #pragma unroll
     for (int end = 0; end < 2; ++end) {
         const int a = end ? N : 0;
@@ -721,14 +731,24 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
             Y.u2 = X.u2 - un2 * X.n2;
             Y.u3 = X.u3 - un2 * X.n3;
         } else if (nb >= 0 && nb < nelem) {
-            Y = F.template partner<PSPLIT>(end, P);
+            Y = F.template partner<PSPLIT, false>(end, P);
             Y.n1 = X.n1; Y.n2 = X.n2; Y.n3 = X.n3;
         } else {
             Y.rho = T(__builtin_nan(""));  // invalid neighbour index: the result says so
         }
         const T coef = end ? T(kEnd) : T(-kEnd);
         T partner[5] = {T(0), T(0), T(0), T(0), T(0)};
-        pair_update<T, false, PSPLIT>(X, Y, &coef, &coef, acc[a], partner, P);
+        const bool series = fabs(Y.rho - X.rho) < eps * (X.rho + Y.rho) &&
+                            fabs(Y.b - X.b) < eps * (X.b + Y.b);
+        if (__all(series)) {
+            pair_update<T, true, PSPLIT>(X, Y, &coef, &coef, acc[a], partner, P);
+        } else {
+            if (nb >= 0 && nb < nelem) {  // the mirror state keeps the own node's logs
+                Y.lrho = A::node_log(Y.rho);
+                Y.lb = A::node_log(Y.b);
+            }
+            pair_update<T, false, PSPLIT>(X, Y, &coef, &coef, acc[a], partner, P);
+        }
     }
 }
 
