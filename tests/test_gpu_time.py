@@ -236,6 +236,25 @@ def test_rhs_pert_every_order(N):
         assert max(by_mag) <= TOL[dtype], (N, dtype, by_mag)
 
 
+@pytest.mark.parametrize("N,K", [(3, (7, 1, 1)), (4, (7, 1, 1)), (4, (5, 1, 2)), (5, (3, 1, 1))])
+def test_rhs_pert_ragged_meshes(N, K):
+    """Perturbation variables on meshes whose last workgroup is partly empty
+    (3 or 4 elements per workgroup at N = 3, 4; 2 at N = 5): every element's
+    reference pressure comes from its own middle node, in both precisions."""
+    q, phi, geom, D, nbr, _ = random_closed_mesh(N, K, (True, True, True), seed=40 + N + K[0])
+    X = I.box_mesh(K, (0, 0, 0), tuple(1000.0 * k for k in K), N, warp_frac=0.05, seed=40 + N + K[0])
+    qp, ref = perturbed(q, phi, X.reshape(3, X.shape[1], -1))
+    for dtype in (np.float64, np.float32):
+        a = [x.astype(dtype) for x in (qp, ref, phi, geom, D)]
+        got = gpu_rhs_pert(*a, nbr)
+        full = oracle.full_state(a[0], a[1], a[2])
+        want, mag = oracle.rhs(full, a[2], a[3], a[4], nbr, N, with_magnitude=True)
+        by_mag, _ = rhs_errors(got, want, mag)
+        print(f"[pert] ragged N={N} K={K} {np.dtype(dtype).name}: err/max mag "
+              f"{['%.1e' % e for e in by_mag]}", flush=True)
+        assert max(by_mag) <= TOL[dtype], (N, K, dtype, by_mag)
+
+
 def test_fp32_noise_full_against_perturbation_variables():
     """The measurement the page's remark calls for ([ESDG-GPU §5.2]): the fp32
     whole right-hand side of the near-balanced bubble against the oracle on
