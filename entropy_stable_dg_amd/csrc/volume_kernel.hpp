@@ -53,7 +53,10 @@
 // entropy-conservative face flux with each end's partner in the neighbouring
 // element (or the mirror state at a slip wall) to that end's accumulator
 // ([ESDG-GPU §3, Eq. 2], surface part); the Coriolis source of Eq. 1b is
-// added at the store.
+// added at the store, and a low-storage Runge-Kutta stage can be fused into
+// that store (Sink).  The measurement probes launch the same kernel with
+// phase marks (WallMarks); the library's instances take NoMarks, which
+// compiles to nothing.
 //
 // On perturbation variables in fp32 (the page's cure for 32-bit noise,
 // [ESDG-GPU §5.2]) the momentum flux's pressure mean is formed relative to
