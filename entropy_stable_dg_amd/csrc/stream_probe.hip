@@ -172,7 +172,7 @@ extern "C" {
 
 int64_t esdg_probe_timeline_workgroups(int N, int64_t nelem, int fp64)
 {
-    if (N < 1 || N > 8 || nelem < 0) return -3;
+    if (N < 1 || N > 8 || nelem < 0 || nelem > INT64_MAX / 2) return -3;
     return fp64 ? workgroups_of<double>(N, nelem) : workgroups_of<float>(N, nelem);
 }
 

@@ -41,6 +41,7 @@ int main(void)
     if (esdg_probe_timeline_workgroups(4, 4096, 0) != 1366) fails++;
     if (esdg_probe_timeline_workgroups(7, 13824, 1) != 13824) fails++;
     if (esdg_probe_timeline_workgroups(9, 10, 1) != -3) fails++;
+    if (esdg_probe_timeline_workgroups(4, (int64_t)0x7fffffffffffffffLL, 1) != -3) fails++;
     if (esdg_probe_timeline_f64(p, p, p, p, 0, 9, 1, r, (uint64_t *)r, 0) != -3) fails++;
     if (esdg_probe_timeline_f64(p, p, p, p, 0, 4, 1, r, (uint64_t *)0, 0) != -1) fails++;
     if (esdg_probe_timeline_f32(0, 0, 0, 0, 0, 4, 0, 0, 0, 0) != 0) fails++;
