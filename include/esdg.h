@@ -124,8 +124,12 @@ int esdg_rhs_f32(const float *q, const float *phi, const float *geom,
  * and the result is the right-hand side of the full state
  * (rbar + qp0, qp1, qp2, qp3, Ebar + qp4).  The kernel forms the pressure as
  * pbar + (gamma-1)(qp4 - |U|^2/(2 rho) - qp0 phi), so the reference's share
- * never enters the subtraction.  rhs must not overlap ref either; ref == NULL
- * gives ESDG_ERR_NULL.  Everything else as esdg_rhs_f64.
+ * never enters the subtraction.  The fp32 entry also forms the momentum
+ * flux's pressure mean relative to each element's reference pressure (pbar
+ * at its node (N/2, N/2, N/2)) and adds that constant's share per node in
+ * fp64: the same result in exact arithmetic, with the rounding of O(p)
+ * pair fluxes taken out of near-balanced states.  rhs must not overlap ref
+ * either; ref == NULL gives ESDG_ERR_NULL.  Everything else as esdg_rhs_f64.
  */
 int esdg_rhs_pert_f64(const double *qp, const double *ref, const double *phi, const double *geom,
                       const double *D, const int32_t *nbr, const double *omega, int N,
