@@ -94,6 +94,18 @@ def test_argument_errors(fn):
     assert fn(0, 0, 0, 0, 3, -1, 0, 0) == esdg.ESDG_ERR_NELEM
 
 
+@pytest.mark.parametrize("fn", [esdg.esdg_volume_rhs_f64, esdg.esdg_volume_rhs_f32])
+def test_grid_limit(fn):
+    # more workgroups than a launch grid holds (2^31 - 1 at 16 elements per
+    # workgroup for N = 1): refused before any HIP call; the fake arrays lie
+    # 2^45 bytes apart so that they do not overlap
+    big = 16 * 2 ** 31 + 16
+    far = [(i + 1) << 45 for i in range(5)]
+    assert fn(far[0], far[1], far[2], far[3], 1, big, far[4], 0) == esdg.ESDG_ERR_NELEM
+    assert esdg.esdg_rhs_f64(far[0], far[1], far[2], far[3], 1 << 40, None, 1, big, far[4],
+                             0) == esdg.ESDG_ERR_NELEM
+
+
 @pytest.mark.parametrize("fn,size", [(esdg.esdg_volume_rhs_f64, 8), (esdg.esdg_volume_rhs_f32, 4)])
 def test_alias_errors(fn, size):
     N, nelem = 3, 100
