@@ -129,6 +129,36 @@ def test_whole_rhs_forms_agree(N, dtype):
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("N", [3, 4, 7])
+def test_face_pair_forms_agree(N, dtype):
+    """The whole right-hand side forms a face partner's logs, and takes the
+    general form of its face pair, only in waves where some face pair is
+    outside the series threshold.  A 50 % jump at one face node of element e
+    (on its +xi1 face) sends the waves of its neighbour across that face to
+    the general form for that end; every element other than e and its face
+    neighbours, in those waves or not, keeps bitwise its clean result, the
+    neighbour's result changes, and both runs meet the parity bar."""
+    q, phi, geom, D, nbr = smooth_workload(N, dtype)
+    nelem, Nq = q.shape[1], N + 1
+    e = 37 % nelem
+    node = N + Nq * (N // 2 + Nq * (N // 2))        # a = N, b = c = N/2
+    partner = int(nbr[e][1])
+    assert partner >= 0
+    qp = perturb(q, e, node)
+    base = run(q, phi, geom, D, nbr)
+    pert = run(qp, phi, geom, D, nbr)
+    touched = {e} | {int(n) for n in nbr[e] if n >= 0}
+    keep = np.array([i not in touched for i in range(nelem)])
+    print(f"[series] face pair N={N} {np.dtype(dtype).name}: element {e} node {node}, "
+          f"partner {partner} changed {not np.array_equal(base[:, partner], pert[:, partner])}",
+          flush=True)
+    assert not np.array_equal(base[:, partner], pert[:, partner])
+    assert np.array_equal(base[:, keep], pert[:, keep])
+    held_to_oracle(base, q, phi, geom, D, N, TOL[dtype], nbr)
+    held_to_oracle(pert, qp, phi, geom, D, N, TOL[dtype], nbr)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("N", [4, 7])
 def test_nan_state_stays_on_its_lines(N, dtype):
     """A NaN in one node's state reaches exactly the nodes that share one of
