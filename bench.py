@@ -747,6 +747,24 @@ def main() -> int:
 
     roofline, binding = roofline_of(achieved_gbs, gflops, stream_gbs, traffic)
 
+    # lower bounds from this run's stream bandwidth and the committed VALU
+    # counts (same kernel code): near their sum when load and compute serialise
+    def floors_of(key, dtype, nbytes, us):
+        v = measured_counter(key.replace(":", "_"), dtype, "valu_wave_instructions_per_launch")
+        return perfmodel.phase_floors(nbytes, v, stream_gbs, us) if v else None
+
+    phase_floors = floors_of(HEADLINE, info["dtype"], info["bytes"], t_cold * 1e6)
+    if phase_floors and binding.startswith("neither"):
+        binding += (f"; the launch takes {phase_floors['measured_over_sum']:.2f} of the sum of its "
+                    f"HBM floor ({phase_floors['hbm_us']:.1f} us at the measured stream) and VALU "
+                    f"issue floor ({phase_floors['valu_us']:.1f} us): its load and compute phases "
+                    + ("barely overlap" if phase_floors["measured_over_sum"] >= 0.9
+                       else "overlap in part"))
+    for key, e in extra.items():
+        if ":" not in key or key.endswith(":rhs"):
+            nbytes = e["hbm_gbs_algorithmic"] * e["us_per_step"] * 1e3
+            e["phase_floors"] = floors_of(key, e["dtype"], nbytes, e["us_per_step"])
+
     # where the headline launch's time goes: phase marks of the same kernel
     # (libesdg_probe), the launch with the median span of five
     timeline = None
@@ -801,6 +819,7 @@ def main() -> int:
                                           if counted_flops else None),
         "hbm_gbs_counted": traffic / t_cold / 1e9 if traffic else None,
         "binding_roof": binding,
+        "phase_floors": phase_floors,
         "phase_timeline": timeline,
         "arithmetic_intensity": perfmodel.arithmetic_intensity(info["N"], info["dtype"]),
         "hot_ms_per_step": t_hot * 1e3,

@@ -81,6 +81,25 @@ PEAK_FP64_VECTOR_TFLOPS = 78.6
 PEAK_FP32_VECTOR_TFLOPS = 157.3
 CU_COUNT = 256
 CLOCK_GHZ = 2.4
+# VALU issue: 256 CUs x 4 SIMDs, 2.4 GHz; a wave64 fp64 or (unpacked) fp32
+# VALU instruction occupies its SIMD for 4 cycles (16 lanes per cycle), which
+# is where the vector peaks come from (78.6 TF/s = 1024 x 16 x 2 x 2.4 GHz)
+SIMDS = 4 * CU_COUNT
+CYCLES_PER_WAVE_VALU = 4
+
+
+def phase_floors(bytes_per_launch: float, valu_wave_instructions: float, stream_gbs: float,
+                 measured_us: float) -> dict:
+    """Two lower bounds on a launch: moving its algorithmic bytes at the
+    measured stream bandwidth, and issuing its counted VALU wave-instructions
+    on every SIMD back to back (4 cycles each, transcendentals counted as one
+    issue).  A kernel whose load and compute phases overlap perfectly runs
+    near the larger; one whose phases serialise, near their sum."""
+    hbm = bytes_per_launch / (stream_gbs * 1e9) * 1e6
+    valu = valu_wave_instructions * CYCLES_PER_WAVE_VALU / (SIMDS * CLOCK_GHZ * 1e9) * 1e6
+    return {"hbm_us": hbm, "valu_us": valu, "max_us": max(hbm, valu), "sum_us": hbm + valu,
+            "measured_us": measured_us, "measured_over_sum": measured_us / (hbm + valu),
+            "measured_over_max": measured_us / max(hbm, valu)}
 
 
 def pairs_per_element(N: int) -> int:

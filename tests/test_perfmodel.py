@@ -31,3 +31,17 @@ def test_per_dof_figures():
     assert P.flops_per_dof(4) == 621.0
     assert abs(P.arithmetic_intensity(4, "f64") - 621.0 / 168.0) < 1e-12
     assert P.bytes_per_dof("f64") == 168 and P.bytes_per_dof("f32") == 84
+
+
+def test_phase_floors():
+    from entropy_stable_dg_amd import perfmodel as P
+
+    # the issue model reproduces the published fp64 vector peak: 1024 SIMDs
+    # x 16 lanes per cycle x 2 FLOP per FMA x 2.4 GHz
+    lanes_per_cycle = 64 / P.CYCLES_PER_WAVE_VALU
+    assert abs(P.SIMDS * lanes_per_cycle * 2 * P.CLOCK_GHZ / 1e3 - P.PEAK_FP64_VECTOR_TFLOPS) < 0.1
+    f = P.phase_floors(86.016e6, 5.65e6, 5000.0, 25.0)
+    assert abs(f["hbm_us"] - 17.2032) < 1e-9
+    assert abs(f["valu_us"] - 5.65e6 * 4 / (1024 * 2.4e9) * 1e6) < 1e-9
+    assert f["sum_us"] == f["hbm_us"] + f["valu_us"] and f["max_us"] == f["hbm_us"]
+    assert abs(f["measured_over_sum"] - 25.0 / f["sum_us"]) < 1e-12
