@@ -183,7 +183,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
           int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
           int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0,
-          int LANES_ = 1>
+          int LANES_ = 1, bool DISTINCT_ = false>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -218,6 +218,11 @@ struct LaunchCfg {
     // LANES = 2: two adjacent lanes share a line, each owning half its nodes
     // (line_pairs_x2); otherwise one lane per line.
     static constexpr int kLanes = LANES_;
+    // DISTINCT: the general form of the pair loop forms the pair's metric
+    // sums as exact fma(x, 1, y) with an opaque 1 (pair_update), so that
+    // where both forms are compiled the compiler finds no common
+    // instructions to hoist above the form branch.
+    static constexpr bool kDistinctSums = DISTINCT_;
 };
 
 template <int N, class C>
@@ -320,11 +325,15 @@ __device__ inline T two_atanh_over_s(T f)
 // PSPLIT: the momentum flux takes the pressure mean relative to the
 // element's reference pressure P (pressure_reference), from the staged
 // b (p - P); the energy flux keeps its whole pressure mean.
-template <typename T, bool SERIES = false, bool PSPLIT = false>
+template <typename T, bool SERIES = false, bool PSPLIT = false, bool DISTINCT = false>
 __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
                                    const T *__restrict__ Dal_p, const T *__restrict__ Dla_p,
                                    T *acc_a, T *acc_l, T P = T(0))
 {
+    // Every fused multiply-add is written out: the two forms of the pair
+    // loop (and the face pairs) are compiled separately and must round
+    // identically, so the compiler may not contract on its own.
+#pragma clang fp contract(off)
     using A = Arith<T>;
     const T eps = T(A::kSeries);
     const T lnk = T(A::kLogToLn);
@@ -370,10 +379,26 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     // = (b_a (p_a - P) + b_l (p_l - P)) / (b_a + b_l)
     const T pt = PSPLIT ? (X.bd + Y.bd) * isb : half_bscale * sr * isb;
     // metric of the pair: Ja^k(a) + Ja^k(l); {{u}} (staged u is halved)
-    const T c1 = X.n1 + Y.n1, c2 = X.n2 + Y.n2, c3 = X.n3 + Y.n3;
+    T c1, c2, c3;
+    if constexpr (!SERIES && DISTINCT) {
+        // The same sums as fma(x, 1, y) (exact: one rounding of x + y) with
+        // a 1 the compiler cannot see through.  Where a kernel carries both
+        // forms, identical sums in both would be hoisted above the form
+        // branch, making the sums of every pair of the line live there at
+        // once (spills in the general form of the fp64 N = 4 whole rhs).
+        T one = T(1);
+        asm volatile("" : "+s"(one));
+        c1 = fma(X.n1, one, Y.n1);
+        c2 = fma(X.n2, one, Y.n2);
+        c3 = fma(X.n3, one, Y.n3);
+    } else {
+        c1 = X.n1 + Y.n1;
+        c2 = X.n2 + Y.n2;
+        c3 = X.n3 + Y.n3;
+    }
     const T s1 = X.u1 + Y.u1, s2 = X.u2 + Y.u2, s3 = X.u3 + Y.u3;
     // contravariant density flux {{rho}}_log ({{u}} . c)
-    const T cs = c1 * s1 + c2 * s2 + c3 * s3;
+    const T cs = fma(c1, s1, fma(c2, s2, c3 * s3));
     const T Fr = Lr * cs;
     // symmetric momentum part S~_m = F~rho {{u_m}} + c_m {{rho}}/(2{{b}})
     const T S1 = fma(Fr, s1, c1 * pt);
@@ -383,7 +408,7 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     // with -{{|u|^2}}/2 + {{phi}} = {{w}} (staged w is halved)
     // (split: S~ lacks c P, so {{u}} . S~ lacks P ({{u}} . c), added back here)
     const T coef = fma(cE, iLb, X.w + Y.w);
-    const T uS = s1 * S1 + s2 * S2 + s3 * S3;
+    const T uS = fma(s1, S1, fma(s2, S2, s3 * S3));
     const T FE = fma(coef, Fr, PSPLIT ? fma(P, cs, uS) : uS);
     // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
     // = (s_b b_a + s_b b_l) {{rho}}_log [[phi/4]] / (s_b b_own)  (staged phi is phi/4)
@@ -570,6 +595,9 @@ template <typename T, bool PERT = false, bool PSPLIT = false, bool LOGS = true>
 __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rbar = T(0),
                                           T pbar = T(0), T P = T(0))
 {
+    // fused multiply-adds written out, as in pair_update: a face partner's
+    // values must round exactly as its own element's staged values
+#pragma clang fp contract(off)
     using A = Arith<T>;
     const T gm1 = T(kGamma - 1.0);
     const T bscale = T(kBScale);
@@ -581,8 +609,8 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
     V.u1 = m1 * hirho;                                  // u/2
     V.u2 = m2 * hirho;
     V.u3 = m3 * hirho;
-    const T usq4 = V.u1 * V.u1 + V.u2 * V.u2 + V.u3 * V.u3;  // |u|^2 / 4
-    const T dE = E - (m1 * V.u1 + m2 * V.u2 + m3 * V.u3) - r * ph;
+    const T usq4 = fma(V.u1, V.u1, fma(V.u2, V.u2, V.u3 * V.u3));  // |u|^2 / 4
+    const T dE = fma(-r, ph, E - fma(m1, V.u1, fma(m2, V.u2, m3 * V.u3)));
     const T p = PERT ? fma(gm1, dE, pbar) : gm1 * dE;
     V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
     V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
@@ -804,8 +832,8 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
         for (int a = 0; a < Nq - 1; ++a)
 #pragma unroll
             for (int l = a + 1; l < Nq; ++l)
-                pair_update<T, SERIES, PSPLIT>(V[a], V[l], D + a * Nq + l, D + l * Nq + a,
-                                               acc[a], acc[l], P);
+                pair_update<T, SERIES, PSPLIT, C::kDistinctSums>(V[a], V[l], D + a * Nq + l,
+                                                                 D + l * Nq + a, acc[a], acc[l], P);
         return;
     }
 #pragma unroll
@@ -831,8 +859,8 @@ __device__ inline void line_pairs_form(const T *lds, const T *__restrict__ D,
             } else {
                 Y.n1 = lm[l][0]; Y.n2 = lm[l][1]; Y.n3 = lm[l][2];
             }
-            pair_update<T, SERIES, PSPLIT>(X, Y, D + a * Nq + l, D + l * Nq + a, acc[a], acc[l],
-                                           P);
+            pair_update<T, SERIES, PSPLIT, C::kDistinctSums>(X, Y, D + a * Nq + l, D + l * Nq + a,
+                                                             acc[a], acc[l], P);
         }
     }
 }
@@ -1150,8 +1178,11 @@ struct Sink {
                 q_out[f * fstride + g] = fma(b, k[f], U[f]);
             }
         } else {
+            // Nothing reads the right-hand side back within the launch: it
+            // streams past the caches (the stage's outputs above stay cached
+            // for the next stage, which reads them).
 #pragma unroll
-            for (int f = 0; f < 5; ++f) out[f * fstride + g] = r[f];
+            for (int f = 0; f < 5; ++f) __builtin_nontemporal_store(r[f], &out[f * fstride + g]);
         }
     }
 };

@@ -19,7 +19,9 @@ PARTIAL_VALUES = 15  # 3 directions x 5 fields
 
 
 def launch_table():
-    """{(dtype, N): (EPB, NT, metric_in_lds, direction_major, finish_in_line)} from launch_table.hpp."""
+    """{(dtype, N): (EPB, NT, metric_in_lds, line order, finish_in_line)} from launch_table.hpp;
+    line order 0 element-major, 1 direction-major, 2 direction-major with each
+    direction on a 32-lane boundary."""
     text = open(API).read()
     rows = re.findall(r"struct Launch<(double|float), (\d+)>\s*\{\s*using C = LaunchCfg<([^>]*)>;", text)
     table = {}
@@ -27,10 +29,28 @@ def launch_table():
         parts = [a.strip() for a in args.split(",")]
         epb, nt = int(parts[0]), int(parts[1])
         metric = parts[3] != "false" if len(parts) > 3 else True
-        dirmajor = parts[5] == "true" if len(parts) > 5 else False
+        kmajor = {"true": 1, "false": 0}.get(parts[5], None) if len(parts) > 5 else 0
+        if kmajor is None:
+            kmajor = int(parts[5])
         fin = parts[6] == "true" if len(parts) > 6 else False
-        table[(dt, int(n))] = (epb, nt, metric, dirmajor, fin)
+        table[(dt, int(n))] = (epb, nt, metric, kmajor, fin)
     return table
+
+
+def line_task(task, EPB, Nq2, kmajor):
+    """(element in batch, direction, line) of a line thread, as LineTask maps it;
+    returns the number of task threads too (threads at or past it are idle)."""
+    lines = 3 * EPB * Nq2
+    if kmajor:
+        stride = (EPB * Nq2 + 31) // 32 * 32 if kmajor == 2 else EPB * Nq2
+        k, r = divmod(task, stride)
+        eb, line = divmod(r, Nq2)   # r past the direction's lines gives eb >= EPB: idle
+        if k > 2:
+            k, eb = 2, EPB
+        return eb, k, line, 3 * stride
+    eb, r3 = divmod(task, 3 * Nq2)
+    k, line = divmod(r3, Nq2)
+    return eb, k, line, lines
 
 
 def test_launch_table_covers_orders():
@@ -52,7 +72,7 @@ def test_staged_value_count_matches_kernel():
 @pytest.mark.parametrize("N", range(1, 9))
 @pytest.mark.parametrize("nelem", [1, 2, 5, 13])
 def test_indices_in_bounds(dtype, N, nelem):
-    EPB, NT, metric_in_lds, dirmajor, fin = launch_table()[(dtype, N)]
+    EPB, NT, metric_in_lds, kmajor, fin = launch_table()[(dtype, N)]
     Nq = N + 1
     Nq2, Np = Nq * Nq, Nq ** 3
     NODES = EPB * Np
@@ -87,22 +107,12 @@ def test_indices_in_bounds(dtype, N, nelem):
                     out_written[g] += 1
         # phase B / C: line threads
         for task in range(NT):
-            if dirmajor:
-                k = task // (EPB * Nq2)
-                r = task - k * EPB * Nq2
-                eb = r // Nq2
-                line = r - eb * Nq2
-                if k > 2:
-                    k, eb = 2, EPB
-            else:
-                eb = task // (3 * Nq2)
-                r3 = task - eb * 3 * Nq2
-                k = r3 // Nq2
-                line = r3 - k * Nq2
+            eb, k, line, task_threads = line_task(task, EPB, Nq2, kmajor)
+            assert task_threads <= NT
             p1, p2 = line % Nq, line // Nq
             base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
             step = [1, Nq, Nq2][k]
-            active = task < lines and eb * Np < nvalid
+            active = task < task_threads and eb * Np < nvalid
             if not active:
                 continue
             nb = eb * Np + base
@@ -140,12 +150,11 @@ def test_face_partner_indices(dtype, N, K, periodic):
     (element, face, face node) is handled by exactly one line end."""
     from entropy_stable_dg_amd import inputs as I
 
-    EPB, NT, _, dirmajor, _ = launch_table()[(dtype, N)]
+    EPB, NT, _, kmajor, _ = launch_table()[(dtype, N)]
     Nq = N + 1
     Nq2, Np = Nq * Nq, Nq ** 3
     nbr = I.box_connectivity(K, periodic)
     nelem = nbr.shape[0]
-    lines = 3 * EPB * Nq2
     blocks = (nelem + EPB - 1) // EPB
     seen = np.zeros((nelem, 6, Nq2), dtype=int)
 
@@ -155,19 +164,8 @@ def test_face_partner_indices(dtype, N, K, periodic):
     for blk in range(blocks):
         nvalid = min(EPB, nelem - blk * EPB) * Np
         for task in range(NT):
-            if dirmajor:
-                k = task // (EPB * Nq2)
-                r = task - k * EPB * Nq2
-                eb = r // Nq2
-                line = r - eb * Nq2
-                if k > 2:
-                    k, eb = 2, EPB
-            else:
-                eb = task // (3 * Nq2)
-                r3 = task - eb * 3 * Nq2
-                k = r3 // Nq2
-                line = r3 - k * Nq2
-            if not (task < lines and eb * Np < nvalid):
+            eb, k, line, task_threads = line_task(task, EPB, Nq2, kmajor)
+            if not (task < task_threads and eb * Np < nvalid):
                 continue
             p1, p2 = line % Nq, line // Nq
             base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
