@@ -33,12 +33,15 @@ namespace esdg {
 // and at fp32 N = 7 and 8 direction-3 lines that finish their nodes (25 and
 // 32 KB of LDS) with 4-wave caps (128 registers) give five and four
 // workgroups per CU instead of four and three.  At fp64 N = 4 and 5 and fp32
-// N = 5 the general pair form forms its metric sums so that the compiler
-// cannot hoist them above the form branch: at fp64 N = 4 the whole rhs's
+// N = 4 and 5 the general pair form forms its metric sums so that the
+// compiler cannot hoist them above the form branch: at fp64 N = 4 the whole rhs's
 // spill falls from 108 to 28 bytes, none left in the series form (1.4x on the
 // rough baroclinic state, 1 % slower on the smooth bubble), and at fp64 N = 5
 // the volume term's 36-byte spill goes (1.10x on the baroclinic state); the
-// other orders measured neutral to slower with it.
+// other orders measured neutral to slower with it.  With it the fp32 N = 4
+// volume term fits 6 waves per SIMD (79 registers, no spill): six workgroups
+// per CU, the 4096-element bubble in one round (1-2 % faster from 10,240
+// elements up, unchanged on the bubble).
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
@@ -57,7 +60,7 @@ template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, fal
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };
 template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, 1, false, true, true, 0, 3, 4>; };
-template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 5>; };
+template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 6, false, false, true, false, true, true, 0, 0, 0, 5, 1, true>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5, 1, true>; };
 template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 4, false, false, 1, true, true, true, 1, 0, 0, 4>; };
