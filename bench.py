@@ -621,8 +621,8 @@ def main() -> int:
                          "high_order; a ':rhs' suffix profiles the whole right-hand side, "
                          "':two_lane' the two-lanes-per-line variant, ':stage' the fused "
                          "Runge-Kutta stage, ':stage_pert' the same in perturbation variables)")
-    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,high_order,"
-                                       "high_order:two_lane",
+    ap.add_argument("--extra", default="bubble_f32,bubble:rhs,bubble_f32:rhs,baroclinic,"
+                                       "baroclinic:rhs,high_order,high_order:two_lane",
                     help="comma-separated extra workloads to time (reported under 'extra'); "
                          "a ':rhs' suffix times the whole right-hand side (volume + surface), "
                          "':graph' replays the launches from a captured HIP graph")
