@@ -41,14 +41,19 @@ namespace esdg {
 // other orders measured neutral to slower with it.  With it the fp32 N = 4
 // volume term fits 6 waves per SIMD (79 registers, no spill): six workgroups
 // per CU, the 4096-element bubble in one round (1-2 % faster from 10,240
-// elements up, unchanged on the bubble).
+// elements up, unchanged on the bubble).  At fp32 N = 4 and 6 the staged
+// value arrays start 64 slots apart (2.4 % and 12 % more LDS, occupancy
+// unchanged), so a node's values come two per ds_read2st64_b32: half the LDS
+// read instructions, 1.6-3.1 % faster; in fp64 the paired reads measured
+// 2-5 % slower, and at fp32 N = 8 the change cost the fourth wave.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
 // with each direction on a 32-lane boundary), direction-3 lines finish the
 // nodes, series form (volume term), series form (with the surface term), LDS
 // pad per row, per plane, per element, waves hint with the surface term,
-// lanes per line, distinct metric sums in the general form>
+// lanes per line, distinct metric sums in the general form, value arrays
+// 64 slots apart>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };     // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, true, 0, 3, 0, 3>; };          // 192/192
@@ -60,9 +65,9 @@ template <> struct Launch<double, 8> { using C = LaunchCfg<1, 256, 0, false, fal
 template <> struct Launch<float, 1> { using C = LaunchCfg<16, 192>; };
 template <> struct Launch<float, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };
 template <> struct Launch<float, 3> { using C = LaunchCfg<4, 192, 0, true, false, 1, false, true, true, 0, 3, 4>; };
-template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 6, false, false, true, false, true, true, 0, 0, 0, 5, 1, true>; };
+template <> struct Launch<float, 4> { using C = LaunchCfg<3, 256, 6, false, false, true, false, true, true, 0, 0, 0, 5, 1, true, true>; };
 template <> struct Launch<float, 5> { using C = LaunchCfg<2, 256, 0, false, false, true, false, true, false, 0, 0, 0, 5, 1, true>; };
-template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true>; };
+template <> struct Launch<float, 6> { using C = LaunchCfg<1, 192, 0, false, false, false, false, true, true, 0, 0, 0, 0, 1, false, true>; };
 template <> struct Launch<float, 7> { using C = LaunchCfg<1, 192, 4, false, false, 1, true, true, true, 1, 0, 0, 4>; };
 template <> struct Launch<float, 8> { using C = LaunchCfg<1, 256, 0, false, false, true, true, true, true, 0, 0, 0, 4>; };
 

@@ -183,7 +183,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
           int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
           int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0,
-          int LANES_ = 1, bool DISTINCT_ = false>
+          int LANES_ = 1, bool DISTINCT_ = false, bool SLOTS64_ = false>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -223,6 +223,10 @@ struct LaunchCfg {
     // where both forms are compiled the compiler finds no common
     // instructions to hoist above the form branch.
     static constexpr bool kDistinctSums = DISTINCT_;
+    // SLOTS64: round the stride between staged value arrays up to a multiple
+    // of 64 slots, so that the compiler can fetch two values of a node with
+    // one ds_read2st64 (offsets in units of 64 elements).
+    static constexpr bool kSlots64 = SLOTS64_;
 };
 
 template <int N, class C>
@@ -236,7 +240,8 @@ struct Shape {
     static constexpr int kPlane = Nq * kRow + C::kPlanePad;
     static constexpr int kElem = Nq * kPlane + C::kElemPad;
     static constexpr bool kPadded = kElem != Np;
-    static constexpr int kSlots = C::EPB * kElem;       // LDS slots per staged value
+    // LDS slots per staged value (the stride between value arrays)
+    static constexpr int kSlots = C::kSlots64 ? (C::EPB * kElem + 63) / 64 * 64 : C::EPB * kElem;
     static constexpr int kLines = 3 * C::EPB * Nq2;     // line tasks per workgroup
     // thread-index stride between the directions' first line tasks
     static constexpr int kDirStride = C::kDirAligned ? (C::EPB * Nq2 + 31) / 32 * 32 : C::EPB * Nq2;

@@ -24,10 +24,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "launch_table.hpp")
 
 # LaunchCfg<EPB, NT, WAVES, METRIC_LDS, CACHE, KMAJOR, FIN, SERIES, SERIES_SURF,
-#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES, DISTINCT> and its defaults
+#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES, DISTINCT, SLOTS64> and its defaults
 FIELDS = ("epb", "nt", "waves", "metric_lds", "cache", "kmajor", "fin", "series", "series_surf",
-          "row_pad", "plane_pad", "elem_pad", "waves_surf", "lanes", "distinct")
-DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0)
+          "row_pad", "plane_pad", "elem_pad", "waves_surf", "lanes", "distinct", "slots64")
+DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 0)
 
 # staged values per node (without / with the metric) and partial sums per node
 STAGED_NO_METRIC, STAGED_WITH_METRIC = 10, 19
@@ -70,6 +70,8 @@ class Shape:
         self.P = self.Nq * self.R + c["plane_pad"]
         self.E = self.Nq * self.P + c["elem_pad"]
         self.slots = self.EPB * self.E
+        if c.get("slots64"):   # value arrays 64 slots apart
+            self.slots = (self.slots + 63) // 64 * 64
         self.lines = 3 * self.EPB * self.Nq2
         lines_per_dir = self.EPB * self.Nq2
         self.dir_stride = (lines_per_dir + 31) // 32 * 32 if c["kmajor"] == 2 else lines_per_dir
