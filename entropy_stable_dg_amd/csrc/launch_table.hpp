@@ -45,9 +45,7 @@ namespace esdg {
 // value arrays start 64 slots apart (2.4 % and 12 % more LDS, occupancy
 // unchanged), so a node's values come two per ds_read2st64_b32: half the LDS
 // read instructions, 1.6-3.1 % faster; in fp64 the paired reads measured
-// 2-5 % slower, and at fp32 N = 8 the change cost the fourth wave.  The rhs
-// is stored non-temporally (Sink::put) except at fp64 N = 4, where ordinary
-// stores measured 1-2 % faster (elsewhere the streamed stores gain 2-6 %).
+// 2-5 % slower, and at fp32 N = 8 the change cost the fourth wave.
 template <typename T, int N> struct Launch;
 // LaunchCfg<EPB, NT, waves hint, metric staged in LDS, line cached in
 // registers, line order (0 element-major, 1 direction-major, 2 direction-major
@@ -55,11 +53,11 @@ template <typename T, int N> struct Launch;
 // nodes, series form (volume term), series form (with the surface term), LDS
 // pad per row, per plane, per element, waves hint with the surface term,
 // lanes per line, distinct metric sums in the general form, value arrays
-// 64 slots apart, ordinary (cached) stores of the rhs>
+// 64 slots apart>
 template <> struct Launch<double, 1> { using C = LaunchCfg<16, 192>; };                       // 192/192 lines
 template <> struct Launch<double, 2> { using C = LaunchCfg<7, 192, 0, true, false, 2>; };     // 189/192
 template <> struct Launch<double, 3> { using C = LaunchCfg<4, 192, 0, false, false, false, false, true, true, 0, 3, 0, 3>; };          // 192/192
-template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 3, 1, true, false, true>; };  // 225/256
+template <> struct Launch<double, 4> { using C = LaunchCfg<3, 256, 0, false, false, true, false, true, true, 0, 0, 0, 3, 1, true>; };  // 225/256
 template <> struct Launch<double, 5> { using C = LaunchCfg<2, 256, 3, false, false, true, false, true, true, 0, 0, 0, 0, 1, true>; };  // 216/256
 template <> struct Launch<double, 6> { using C = LaunchCfg<1, 192, 0, true, false, 2, false, true, true, 0, 0, 0, 3>; };          // 147/192
 template <> struct Launch<double, 7> { using C = LaunchCfg<1, 192, 0, false, false, true, true, true, true, 1>; };      // 192/192

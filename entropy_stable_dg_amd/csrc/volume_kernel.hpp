@@ -183,8 +183,7 @@ constexpr int kPartialValues = 15;  // 3 directions x 5 fields
 template <int EPB_, int NT_, int WAVES_ = 0, bool METRIC_LDS_ = true, bool CACHE_ = false,
           int KMAJOR_ = 0, bool FIN_ = false, bool SERIES_ = false, bool SERIES_SURF_ = false,
           int ROW_PAD_ = 0, int PLANE_PAD_ = 0, int ELEM_PAD_ = 0, int WAVES_SURF_ = 0,
-          int LANES_ = 1, bool DISTINCT_ = false, bool SLOTS64_ = false,
-          bool CACHED_OUT_ = false>
+          int LANES_ = 1, bool DISTINCT_ = false, bool SLOTS64_ = false>
 struct LaunchCfg {
     static constexpr int EPB = EPB_;
     static constexpr int NT = NT_;
@@ -228,9 +227,6 @@ struct LaunchCfg {
     // of 64 slots, so that the compiler can fetch two values of a node with
     // one ds_read2st64 (offsets in units of 64 elements).
     static constexpr bool kSlots64 = SLOTS64_;
-    // CACHED_OUT: the right-hand side is stored with ordinary stores instead
-    // of streaming past the caches (Sink::put).
-    static constexpr bool kCachedOut = CACHED_OUT_;
 };
 
 template <int N, class C>
@@ -1165,7 +1161,6 @@ struct Sink {
     T *__restrict__ out;    // rhs, or the register dq with STAGE
     T *__restrict__ q_out;  // STAGE: the stage's output state
     T a, b, dt;             // STAGE: the stage's coefficients and the step
-    template <bool STREAM = true>
     __device__ inline void put(const T *__restrict__ q, int64_t fstride, int64_t g,
                                const Rotation<T> &rot, T (&r)[5]) const {
         T U[5];
@@ -1187,15 +1182,12 @@ struct Sink {
                 out[f * fstride + g] = k[f];
                 q_out[f * fstride + g] = fma(b, k[f], U[f]);
             }
-        } else if constexpr (STREAM) {
+        } else {
             // Nothing reads the right-hand side back within the launch: it
             // streams past the caches (the stage's outputs above stay cached
             // for the next stage, which reads them).
 #pragma unroll
             for (int f = 0; f < 5; ++f) __builtin_nontemporal_store(r[f], &out[f * fstride + g]);
-        } else {
-#pragma unroll
-            for (int f = 0; f < 5; ++f) out[f * fstride + g] = r[f];
         }
     }
 };
@@ -1235,7 +1227,7 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
 #pragma unroll
             for (int f = 0; f < 5; ++f)
                 r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + acc[a][f]) * mJ;
-            sink.template put<!C::kCachedOut>(q, fstride, g, rot, r);
+            sink.put(q, fstride, g, rot, r);
         }
     }
 }
@@ -1260,7 +1252,7 @@ __device__ inline void finish_line_x2(const T *lds, const LineTask<N, C> &L, boo
 #pragma unroll
             for (int f = 0; f < 5; ++f)
                 r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + sg * acc[j][f]) * mJ;
-            sink.template put<!C::kCachedOut>(q, fstride, g, rot, r);
+            sink.put(q, fstride, g, rot, r);
         }
     }
 }
@@ -1283,7 +1275,7 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
                 const T s = lds[f * SLOTS + st] + lds[(5 + f) * SLOTS + st] + lds[(10 + f) * SLOTS + st];
                 r[f] = s * mJ[it];
             }
-            sink.template put<!C::kCachedOut>(q, fstride, g, rot, r);
+            sink.put(q, fstride, g, rot, r);
         }
     }
 }

@@ -24,12 +24,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 API_SOURCE = os.path.join(os.path.dirname(HERE), "entropy_stable_dg_amd", "csrc", "launch_table.hpp")
 
 # LaunchCfg<EPB, NT, WAVES, METRIC_LDS, CACHE, KMAJOR, FIN, SERIES, SERIES_SURF,
-#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES, DISTINCT, SLOTS64, CACHED_OUT>
-# and its defaults
+#           ROW_PAD, PLANE_PAD, ELEM_PAD, WAVES_SURF, LANES, DISTINCT, SLOTS64> and its defaults
 FIELDS = ("epb", "nt", "waves", "metric_lds", "cache", "kmajor", "fin", "series", "series_surf",
-          "row_pad", "plane_pad", "elem_pad", "waves_surf", "lanes", "distinct", "slots64",
-          "cached_out")
-DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 0, 0)
+          "row_pad", "plane_pad", "elem_pad", "waves_surf", "lanes", "distinct", "slots64")
+DEFAULTS = (None, None, 0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 0)
 
 # staged values per node (without / with the metric) and partial sums per node
 STAGED_NO_METRIC, STAGED_WITH_METRIC = 10, 19
