@@ -537,9 +537,21 @@ struct LineTask {
 template <int N>
 constexpr int kPressureNode = (N / 2) * (1 + (N + 1) + (N + 1) * (N + 1));
 
+// A global load, non-temporal with STREAM.
+template <bool STREAM, typename T>
+__device__ inline T load(const T *p)
+{
+    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // Global values one thread loads for phase A: IT nodes x (5 fields, phi,
 // with PERT the reference density and pressure, 9 metric terms when staged,
-// J).
+// J).  STREAM loads the state, phi and J non-temporally: in the volume term
+// alone nothing reads them again, so they need not displace the line
+// threads' metric loads, which revisit their cache lines, from the caches
+// (the whole rhs re-reads neighbours' states for the face partners and
+// keeps ordinary loads).
 template <typename T, int N, class C, bool PERT = false, bool PSPLIT = false>
 struct NodeLoads {
     using S = Shape<N, C>;
@@ -547,6 +559,7 @@ struct NodeLoads {
     T v[IT][PSPLIT ? 9 : PERT ? 8 : 6];
     T m[C::kMetricInLds ? IT : 1][9];
     T J[IT];
+    template <bool STREAM = false>
     __device__ inline void issue(const T *__restrict__ q, const T *__restrict__ ref,
                                  const T *__restrict__ phi, const T *__restrict__ geom,
                                  int64_t fstride, const Batch<N, C> &B) {
@@ -556,8 +569,8 @@ struct NodeLoads {
             if (t < B.nvalid) {
                 const int64_t g = B.g0 + t;
 #pragma unroll
-                for (int f = 0; f < 5; ++f) v[it][f] = q[f * fstride + g];
-                v[it][5] = phi[g];
+                for (int f = 0; f < 5; ++f) v[it][f] = load<STREAM>(&q[f * fstride + g]);
+                v[it][5] = load<STREAM>(&phi[g]);
                 if constexpr (PERT) {
                     v[it][6] = ref[g];
                     v[it][7] = ref[fstride + g];
@@ -570,7 +583,7 @@ struct NodeLoads {
 #pragma unroll
                     for (int j = 0; j < 9; ++j) m[it][j] = geom[j * fstride + g];
                 }
-                J[it] = geom[9 * fstride + g];
+                J[it] = load<STREAM>(&geom[9 * fstride + g]);
             }
         }
     }
@@ -1356,7 +1369,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
             if (active) face.issue_neighbour(nbr, batch * C::EPB + L.eb, L.k, L.half);
         }
         NodeLoads<T, N, C, PERT> ld;
-        ld.issue(q, ref, phi, geom, fstride, B);
+        ld.template issue<!SURF>(q, ref, phi, geom, fstride, B);
         T lm[H][3];
         if (active) {
 #pragma unroll
@@ -1404,7 +1417,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
     }
     NodeLoads<T, N, C, PERT, PSPLIT> ld;
-    ld.issue(q, ref, phi, geom, fstride, B);
+    ld.template issue<!SURF>(q, ref, phi, geom, fstride, B);
     T P = T(0);  // the element's reference pressure (PSPLIT)
     if constexpr (PSPLIT) {
         if (active) P = ref[fstride + B.g0 + L.eb * S::Np + kPressureNode<N>];
