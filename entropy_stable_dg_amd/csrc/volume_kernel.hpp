@@ -20,8 +20,9 @@
 // Work mapping (MI355X-specific; the pages map a thread to a node):
 //   * A workgroup owns EPB consecutive elements.
 //   * Phase A, one thread per node: coalesced SoA loads of the 5 conserved
-//     fields and phi; primitives, p, the scaled b = s_b rho/(2p), the logs
-//     of rho and b and 1/b are computed once per node and staged in LDS.
+//     fields and phi (non-temporal in the volume term alone, where nothing
+//     reads them again); primitives, p, the scaled b = s_b rho/(2p), the
+//     logs of rho and b and 1/b are computed once per node and staged in LDS.
 //     The metric terms Ja^k_j are either staged in LDS too or loaded by each
 //     line thread for its own line straight into registers (a per-order
 //     launch choice).
@@ -35,18 +36,23 @@
 //     of a wave lies within the log means' series threshold (one wave vote,
 //     a per-order launch option), the wave runs a second copy of the pair
 //     loop without the log branch and its selects; both copies give the same
-//     values.
+//     values.  Both copies are compiled into one kernel: where the launch
+//     table asks for it, the general copy forms its pair metric sums with
+//     different instructions, so that the compiler hoists nothing common to
+//     both above the form branch (pair_update).
 //   * LDS layout: field-major, one array per staged value over the node
 //     grid of the workgroup's elements; per-order launch options pad that
 //     grid (per row, plane or element) and start each direction's line
 //     tasks on a 32-lane boundary, so that the lanes of a wave, each reading
-//     one node of its own line, fall on different LDS banks.
+//     one node of its own line, fall on different LDS banks, and may round
+//     the arrays' stride to 64 slots so that two values of a node come with
+//     one paired read.
 //   * Phase C: each line writes its Nq x 5 partial sums to LDS (one array per
 //     direction, every slot written by exactly one thread: no atomics, the
 //     result is bitwise reproducible).
 //   * Phase D, one thread per node: sum of the three directional partials,
-//     scaling by -1/J, coalesced SoA store (or, with FIN, the direction-3
-//     line threads finish their own nodes).
+//     scaling by -1/J, coalesced SoA store, non-temporal (or, with FIN, the
+//     direction-3 line threads finish their own nodes).
 //
 // The whole right-hand side (SURF) reuses this kernel: a line's two end
 // nodes lie on the element's two xi_k faces, so the line thread adds the
