@@ -550,6 +550,29 @@ __device__ inline T load(const T *p)
     if constexpr (STREAM) return __builtin_nontemporal_load(p);
     else return *p;
 }
+template <bool STREAM, typename T>
+__device__ inline T load(__attribute__((address_space(1))) const T *p)
+{
+    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// &p[i] for a workgroup-uniform base p and a lane index 0 <= i with
+// i * sizeof(T) < 2^32, in the form the global memory instructions take
+// natively: a 64-bit base in scalar registers plus a 32-bit lane offset, so
+// no 64-bit address arithmetic runs per lane.  The base passes through
+// readfirstlane (exact for a uniform value), which keeps the compiler from
+// folding it back into per-lane arithmetic.
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T *;
+template <typename T>
+__device__ inline global_ptr<T> lane_at(T *p, int i)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<global_ptr<T>>((hi << 32 | lo) + (uint32_t)i * (uint32_t)sizeof(T));
+}
 
 // Global values one thread loads for phase A: IT nodes x (5 fields, phi,
 // with PERT the reference density and pressure, 9 metric terms when staged,
@@ -573,23 +596,24 @@ struct NodeLoads {
         for (int it = 0; it < IT; ++it) {
             const int t = threadIdx.x + it * C::NT;
             if (t < B.nvalid) {
-                const int64_t g = B.g0 + t;
+                // field bases of the batch are uniform; t is the lane offset
 #pragma unroll
-                for (int f = 0; f < 5; ++f) v[it][f] = load<STREAM>(&q[f * fstride + g]);
-                v[it][5] = load<STREAM>(&phi[g]);
+                for (int f = 0; f < 5; ++f)
+                    v[it][f] = load<STREAM>(lane_at(q + (f * fstride + B.g0), t));
+                v[it][5] = load<STREAM>(lane_at(phi + B.g0, t));
                 if constexpr (PERT) {
-                    v[it][6] = ref[g];
-                    v[it][7] = ref[fstride + g];
+                    v[it][6] = *lane_at(ref + B.g0, t);
+                    v[it][7] = *lane_at(ref + (fstride + B.g0), t);
                 }
                 if constexpr (PSPLIT) {
                     // the element's reference pressure P (pressure_reference)
-                    v[it][8] = ref[fstride + B.g0 + (t / S::Np) * S::Np + kPressureNode<N>];
+                    v[it][8] = *lane_at(ref + (fstride + B.g0), (t / S::Np) * S::Np + kPressureNode<N>);
                 }
                 if constexpr (C::kMetricInLds) {
 #pragma unroll
-                    for (int j = 0; j < 9; ++j) m[it][j] = geom[j * fstride + g];
+                    for (int j = 0; j < 9; ++j) m[it][j] = *lane_at(geom + (j * fstride + B.g0), t);
                 }
-                J[it] = load<STREAM>(&geom[9 * fstride + g]);
+                J[it] = load<STREAM>(lane_at(geom + (9 * fstride + B.g0), t));
             }
         }
     }
@@ -1180,12 +1204,14 @@ struct Sink {
     T *__restrict__ out;    // rhs, or the register dq with STAGE
     T *__restrict__ q_out;  // STAGE: the stage's output state
     T a, b, dt;             // STAGE: the stage's coefficients and the step
-    __device__ inline void put(const T *__restrict__ q, int64_t fstride, int64_t g,
+    // The node is i of the batch that starts at node g0 (uniform).
+    __device__ inline void put(const T *__restrict__ q, int64_t fstride, int64_t g0, int i,
                                const Rotation<T> &rot, T (&r)[5]) const {
         T U[5];
         if (STAGE || rot.on) {
 #pragma unroll
-            for (int f = STAGE ? 0 : 1; f < (STAGE ? 5 : 4); ++f) U[f] = q[f * fstride + g];
+            for (int f = STAGE ? 0 : 1; f < (STAGE ? 5 : 4); ++f)
+                U[f] = *lane_at(q + (f * fstride + g0), i);
         }
         if (rot.on) rot.add(U[1], U[2], U[3], r[1], r[2], r[3]);
         if constexpr (STAGE) {
@@ -1194,19 +1220,20 @@ struct Sink {
             for (int f = 0; f < 5; ++f) k[f] = dt * r[f];
             if (a != T(0)) {
 #pragma unroll
-                for (int f = 0; f < 5; ++f) k[f] = fma(a, out[f * fstride + g], k[f]);
+                for (int f = 0; f < 5; ++f) k[f] = fma(a, *lane_at(out + (f * fstride + g0), i), k[f]);
             }
 #pragma unroll
             for (int f = 0; f < 5; ++f) {
-                out[f * fstride + g] = k[f];
-                q_out[f * fstride + g] = fma(b, k[f], U[f]);
+                *lane_at(out + (f * fstride + g0), i) = k[f];
+                *lane_at(q_out + (f * fstride + g0), i) = fma(b, k[f], U[f]);
             }
         } else {
             // Nothing reads the right-hand side back within the launch: it
             // streams past the caches (the stage's outputs above stay cached
             // for the next stage, which reads them).
 #pragma unroll
-            for (int f = 0; f < 5; ++f) __builtin_nontemporal_store(r[f], &out[f * fstride + g]);
+            for (int f = 0; f < 5; ++f)
+                __builtin_nontemporal_store(r[f], lane_at(out + (f * fstride + g0), i));
         }
     }
 };
@@ -1241,12 +1268,11 @@ __device__ inline void finish_line(const T *lds, const LineTask<N, C> &L, bool a
         for (int a = 0; a < N + 1; ++a) {
             const int s = L.nb + a * L.step;
             const T mJ = lds[Shape<N, C>::kMinusInvJ * SLOTS + s];
-            const int64_t g = B.g0 + L.node(a);
             T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f)
                 r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + acc[a][f]) * mJ;
-            sink.put(q, fstride, g, rot, r);
+            sink.put(q, fstride, B.g0, L.node(a), rot, r);
         }
     }
 }
@@ -1266,12 +1292,11 @@ __device__ inline void finish_line_x2(const T *lds, const LineTask<N, C> &L, boo
             const int a = L.own(j);
             const int s = L.nb + a * L.step;
             const T mJ = lds[Shape<N, C>::kMinusInvJ * SLOTS + s];
-            const int64_t g = B.g0 + L.node(a);
             T r[5];
 #pragma unroll
             for (int f = 0; f < 5; ++f)
                 r[f] = (lds[f * SLOTS + s] + lds[(5 + f) * SLOTS + s] + sg * acc[j][f]) * mJ;
-            sink.put(q, fstride, g, rot, r);
+            sink.put(q, fstride, B.g0, L.node(a), rot, r);
         }
     }
 }
@@ -1286,7 +1311,6 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
     for (int it = 0; it < Shape<N, C>::kNodeIters; ++it) {
         const int t = threadIdx.x + it * C::NT;
         if (t < B.nvalid) {
-            const int64_t g = B.g0 + t;
             const int st = Shape<N, C>::slot(t);
             T r[5];
 #pragma unroll
@@ -1294,7 +1318,7 @@ __device__ inline void store_rhs(const T *lds, const Batch<N, C> &B, int64_t fst
                 const T s = lds[f * SLOTS + st] + lds[(5 + f) * SLOTS + st] + lds[(10 + f) * SLOTS + st];
                 r[f] = s * mJ[it];
             }
-            sink.put(q, fstride, g, rot, r);
+            sink.put(q, fstride, B.g0, t, rot, r);
         }
     }
 }
@@ -1431,11 +1455,16 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     T lm[C::kMetricInLds ? 1 : Nq][3];
     if constexpr (!C::kMetricInLds) {
         if (active) {
+            // the line's Ja^k_1 at its first node: one 64-bit product per lane,
+            // then uniform field offsets and a pointer step along the line
+            const T *p = geom + ((int64_t)(3 * L.k) * fstride + (B.g0 + L.node_base()));
+            const int step = L.node_step();
 #pragma unroll
-            for (int a = 0; a < Nq; ++a)
+            for (int a = 0; a < Nq; ++a) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    lm[a][j] = geom[(3 * L.k + j) * fstride + B.g0 + L.node_base() + a * L.node_step()];
+                for (int j = 0; j < 3; ++j) lm[a][j] = p[j * fstride];
+                p += step;
+            }
         }
     }
     if constexpr (SURF) {
