@@ -160,10 +160,12 @@ __device__ inline void stage(const double *__restrict__ q, const double *__restr
     for (int m = 0; m < 9; ++m) lds[(pJa + m) * G::Np + t] = geom[m * fstride + g];
     lds[pJ * G::Np + t] = geom[9 * fstride + g];
     if (variant >= LOGMEAN) {
-        const double bs = kBScale * b;
+        // b is scaled by 2^17 for its log; the rungs that call the production
+        // pair routine stage 2b (and 1/(2b)) as it expects
+        const double bs = (variant >= CONTRA ? esdg::kBStage : kBScale) * b;
         lds[pBs * G::Np + t] = bs;
         lds[pLRho * G::Np + t] = A::node_log(rho);
-        lds[pLB * G::Np + t] = A::node_log(bs);
+        lds[pLB * G::Np + t] = A::node_log(kBScale * b);
         lds[pW * G::Np + t] = ph - 0.5 * usq;
         lds[pIB * G::Np + t] = 1.0 / bs;
     }

@@ -21,8 +21,8 @@
 //   * A workgroup owns EPB consecutive elements.
 //   * Phase A, one thread per node: coalesced SoA loads of the 5 conserved
 //     fields and phi (non-temporal in the volume term alone, where nothing
-//     reads them again); primitives, p, the scaled b = s_b rho/(2p), the
-//     logs of rho and b and 1/b are computed once per node and staged in LDS.
+//     reads them again); primitives, p, the staged 2b = rho/p, the logs of
+//     rho and b and 1/(2b) are computed once per node and staged in LDS.
 //     The metric terms Ja^k_j are either staged in LDS too or loaded by each
 //     line thread for its own line straight into registers (a per-order
 //     launch choice).
@@ -77,10 +77,13 @@
 namespace esdg {
 
 constexpr double kGamma = 1.4;
-// b = rho/(2p) is O(1e-6) for air; the kernel works with s_b * b where
-// s_b = 2^17 (exact scaling).  {{s b}}_log = s {{b}}_log, so only constants
-// change, while logs and products stay O(1) (this matters in fp32).
+// b = rho/(2p) is O(1e-6) for air.  Logs of b are taken of s_b b with
+// s_b = 2^17 (exact scaling), so they stay O(1) (this matters in fp32).
+// The pairs work with the staged value 2b = rho/p: then a pair's pressure
+// mean {{rho}}/(2{{b}}) is its density sum over its staged-b sum, with no
+// constant factor.  {{s b}}_log = s {{b}}_log, so only constants change.
 constexpr double kBScale = 131072.0;
+constexpr double kBStage = 2.0;
 
 template <typename T> struct Arith;
 
@@ -149,6 +152,13 @@ template <> struct Arith<float> {
     __device__ static inline float node_log(float x) { return __builtin_amdgcn_logf(x); }
     __device__ static inline float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 };
+
+// Log of a node's b from its staged value 2b (the log of 2^17 b).
+template <typename T>
+__device__ inline T b_log(T b_staged)
+{
+    return Arith<T>::node_log(T(kBScale / kBStage) * b_staged);
+}
 
 // Branch-free select of a and b on c.  Both operands are always computed
 // (they are a few multiplies each); a plain ?: lets the compiler sink their
@@ -348,8 +358,7 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     using A = Arith<T>;
     const T eps = T(A::kSeries);
     const T lnk = T(A::kLogToLn);
-    const T cE = T(kBScale / (2.0 * (kGamma - 1.0)));  // s_b/(2(gamma-1))
-    const T half_bscale = T(0.5 * kBScale);
+    const T cE = T(kBStage / (2.0 * (kGamma - 1.0)));  // 2/(2(gamma-1)) for the staged 2b
     // sums and jumps (jumps are partner l minus receiving node a)
     const T sr = X.rho + Y.rho, dr = Y.rho - X.rho;
     const T sb = X.b + Y.b, db = Y.b - X.b;
@@ -382,13 +391,13 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
         // {{rho}}_log: series sr/2 * s/atanh(s) (s = dr/sr), else dr/(ln-difference)
         const T tr = dr * isr;
         Lr = select(ser_r, sr * half_s_over_atanh(tr * tr), dr * iAr);
-        // 1/{{s_b b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
+        // 1/{{2b}}_log: series 2 atanh(s)/s / sb, else (ln-difference)/db
         const T tb = db * isb;
         iLb = select(ser_b, two_atanh_over_s(tb * tb) * isb, lnk * (Y.lb - X.lb) * iBb);
     }
-    // {{rho}}/(2{{b}}) with the b scaling undone; split: {{rho}}/(2{{b}}) - P
+    // {{rho}}/(2{{b}}): the density sum over the staged-2b sum; split: {{rho}}/(2{{b}}) - P
     // = (b_a (p_a - P) + b_l (p_l - P)) / (b_a + b_l)
-    const T pt = PSPLIT ? (X.bd + Y.bd) * isb : half_bscale * sr * isb;
+    const T pt = PSPLIT ? (X.bd + Y.bd) * isb : sr * isb;
     // metric of the pair: Ja^k(a) + Ja^k(l); {{u}} (staged u is halved)
     T c1, c2, c3;
     if constexpr (!SERIES && DISTINCT) {
@@ -422,7 +431,7 @@ __device__ inline void pair_update(const NodeRegs<T> X, const NodeRegs<T> Y,
     const T uS = fma(s1, S1, fma(s2, S2, s3 * S3));
     const T FE = fma(coef, Fr, PSPLIT ? fma(P, cs, uS) : uS);
     // gravity: 1/2 rhohat [[phi]] with rhohat = {{b}}{{rho}}_log / b_own
-    // = (s_b b_a + s_b b_l) {{rho}}_log [[phi/4]] / (s_b b_own)  (staged phi is phi/4)
+    // = (2b_a + 2b_l) {{rho}}_log [[phi/4]] / (2b_own)  (staged phi is phi/4)
     const T g = sb * Lr * (Y.ph - X.ph);
     const T ga = g * X.ib;
     const T gl = -g * Y.ib;
@@ -619,7 +628,7 @@ struct NodeLoads {
     }
 };
 
-// Per-node values the pairs use (primitives, scaled b, logs, 1/b, w), from the
+// Per-node values the pairs use (primitives, 2b, logs, 1/(2b), w), from the
 // conserved state and phi.  Phase A stages them for the element's own nodes;
 // the surface term builds them for the face partners in a neighbouring
 // element with the same operations, so both sides of a face see identical
@@ -648,7 +657,6 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
 #pragma clang fp contract(off)
     using A = Arith<T>;
     const T gm1 = T(kGamma - 1.0);
-    const T bscale = T(kBScale);
     NodeRegs<T> V;
     const T rho = PERT ? rbar + r : r;
     const T irho = A::rcp(rho);
@@ -660,12 +668,12 @@ __device__ inline NodeRegs<T> node_values(T r, T m1, T m2, T m3, T E, T ph, T rb
     const T usq4 = fma(V.u1, V.u1, fma(V.u2, V.u2, V.u3 * V.u3));  // |u|^2 / 4
     const T dE = fma(-r, ph, E - fma(m1, V.u1, fma(m2, V.u2, m3 * V.u3)));
     const T p = PERT ? fma(gm1, dE, pbar) : gm1 * dE;
-    V.b = T(0.5) * bscale * rho * A::rcp(p);      // s_b rho/(2p)
-    V.ib = (T(2) / bscale) * p * irho;            // 1/(s_b b)
+    V.b = rho * A::rcp(p);                        // 2b = rho/p
+    V.ib = p * irho;                              // 1/(2b)
     if constexpr (PSPLIT) V.bd = V.b * fma(gm1, dE, pbar - P);
     if constexpr (LOGS) {
         V.lrho = A::node_log(rho);
-        V.lb = A::node_log(V.b);
+        V.lb = b_log(V.b);
     }
     V.ph = T(0.25) * ph;                          // phi/4
     V.w = fma(T(0.5), ph, -usq4);                 // w/2 = (phi - |u|^2/2)/2
@@ -824,7 +832,7 @@ __device__ inline void surface_ends(const T *lds, const LineTask<N, C> &L,
         } else {
             if (nb >= 0 && nb < nelem) {  // the mirror state keeps the own node's logs
                 Y.lrho = A::node_log(Y.rho);
-                Y.lb = A::node_log(Y.b);
+                Y.lb = b_log(Y.b);
             }
             pair_update<T, false, PSPLIT>(X, Y, &coef, &coef, acc[a], partner, P);
         }

@@ -13,8 +13,8 @@ hoisted per node are counted once per node.  The tallies below follow the
 kernel's pair and node arithmetic step by step (pair_update and node_values
 of csrc/volume_kernel.hpp, series form):
 
-  per unordered pair on a line ........ 96   (PAIR_STEPS)
-  per node ............................ 45   (NODE_STEPS)
+  per unordered pair on a line ........ 95   (PAIR_STEPS)
+  per node ............................ 44   (NODE_STEPS)
 
 Unordered pairs per element: 3 (N+1)^2 (N+1) N / 2.
 
@@ -36,7 +36,7 @@ PAIR_STEPS = (
     ("1/(rho_a+rho_l), 1/(b_a+b_l)", {"mul": 2}),
     ("log mean of rho: s, s^2, cubic series in s^2, scale", {"mul": 3, "fma": 3}),
     ("inverse log mean of b: s, s^2, cubic series in s^2, scale", {"mul": 3, "fma": 3}),
-    ("{{rho}}/(2{{b}})", {"mul": 2}),
+    ("{{rho}}/(2{{b}}): density sum over the staged-2b sum", {"mul": 1}),
     ("pair metric Ja^k(a) + Ja^k(l)", {"add": 3}),
     ("2{{u}}", {"add": 3}),
     ("contravariant density flux", {"mul": 2, "fma": 2}),
@@ -54,9 +54,9 @@ NODE_STEPS = (
     ("|u|^2/4", {"mul": 1, "fma": 2}),
     ("E - U.u/2... - rho phi", {"mul": 1, "fma": 3, "add": 1}),
     ("p", {"mul": 1}),
-    ("scaled b = s_b rho/(2p)", {"rcp": 1, "mul": 2}),
-    ("1/b", {"mul": 2}),
-    ("ln rho, ln b", {"log": 2}),
+    ("staged 2b = rho/p", {"rcp": 1, "mul": 1}),
+    ("1/(2b) = p/rho", {"mul": 1}),
+    ("ln rho, ln b (the log of 2^16 x 2b)", {"log": 2, "mul": 1}),
     ("phi/4", {"mul": 1}),
     ("w/2 = (phi - |u|^2/2)/2", {"fma": 1}),
     ("-1/J", {"rcp": 1}),

@@ -13,23 +13,23 @@ def test_pair_tally():
     for _, ops in P.PAIR_STEPS:
         for op, n in ops.items():
             by_op[op] = by_op.get(op, 0) + n
-    # series form of the pair: 12 adds, 21 multiplies, 31 fused multiply-adds, 1 reciprocal
-    assert by_op == {"add": 12, "mul": 21, "fma": 31, "rcp": 1}
-    assert P.FLOP_PER_PAIR == 12 + 21 + 2 * 31 + 1 == 96
+    # series form of the pair: 12 adds, 20 multiplies, 31 fused multiply-adds, 1 reciprocal
+    assert by_op == {"add": 12, "mul": 20, "fma": 31, "rcp": 1}
+    assert P.FLOP_PER_PAIR == 12 + 20 + 2 * 31 + 1 == 95
 
 
 def test_node_tally():
-    assert P.FLOP_PER_NODE == 45
-    assert P.FLOP_PER_PARTNER_NODE == 45 - 1 - 10 - 5
+    assert P.FLOP_PER_NODE == 44
+    assert P.FLOP_PER_PARTNER_NODE == 44 - 1 - 10 - 5
 
 
 def test_per_dof_figures():
     # pairs per element 3 Nq^2 Nq N/2; per DOF 3N/2
     for N in range(1, 9):
         assert P.pairs_per_element(N) == 3 * (N + 1) ** 3 * N // 2
-        assert abs(P.flops_per_dof(N) - (1.5 * N * 96 + 45)) < 1e-12
-    assert P.flops_per_dof(4) == 621.0
-    assert abs(P.arithmetic_intensity(4, "f64") - 621.0 / 168.0) < 1e-12
+        assert abs(P.flops_per_dof(N) - (1.5 * N * 95 + 44)) < 1e-12
+    assert P.flops_per_dof(4) == 614.0
+    assert abs(P.arithmetic_intensity(4, "f64") - 614.0 / 168.0) < 1e-12
     assert P.bytes_per_dof("f64") == 168 and P.bytes_per_dof("f32") == 84
 
 
