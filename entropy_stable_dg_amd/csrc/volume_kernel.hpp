@@ -603,8 +603,13 @@ struct NodeLoads {
                                  int64_t fstride, const Batch<N, C> &B) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int t = threadIdx.x + it * C::NT;
-            if (t < B.nvalid) {
+            // Every lane loads, one past the batch's nodes the batch's last
+            // node (in bounds, unused): with the loads under a branch the
+            // compiler could not count them, and the later partner loads of
+            // the whole rhs waited for all of them.
+            const int t0 = threadIdx.x + it * C::NT;
+            const int t = t0 < B.nvalid ? t0 : B.nvalid - 1;
+            {
                 // field bases of the batch are uniform; t is the lane offset
 #pragma unroll
                 for (int f = 0; f < 5; ++f)
@@ -739,29 +744,37 @@ template <typename T, bool PERT = false>
 struct FaceLoads {
     int32_t nb[2];   // neighbour across the face at line end 0 (a = 0) and end 1 (a = N)
     T v[2][PERT ? 8 : 6];  // its matching node: 5 conserved fields, phi (and the reference)
-    __device__ inline void issue_neighbours(const int32_t *__restrict__ nbr, int64_t e, int k) {
-        nb[0] = nbr[6 * e + 2 * k];
-        nb[1] = nbr[6 * e + 2 * k + 1];
+    // `nbr_batch` points at the batch's first element's entries (uniform),
+    // `eb` is the lane's element within the batch.
+    __device__ inline void issue_neighbours(const int32_t *__restrict__ nbr_batch, int eb, int k) {
+        nb[0] = *lane_at(nbr_batch, 6 * eb + 2 * k);
+        nb[1] = *lane_at(nbr_batch, 6 * eb + 2 * k + 1);
     }
     // Loads of the matching nodes; `local0` is the line's first node within
-    // its element, `step` the node stride along the line.  Indices outside
-    // [0, nelem) load nothing.
+    // its element, `step` the node stride along the line.  A neighbour index
+    // outside [0, nelem) (a wall, or an invalid index) loads the node of the
+    // lane's own element (first node `own0`) instead, in bounds and unused.
+    // The loads are issued unconditionally: behind a branch, the compiler
+    // could no longer count them and made the node values wait for them too.
+    // The index is non-negative where used, so its product with Np is formed
+    // from 32 bits (a 64-bit product's expansion may read a register a load
+    // is still writing, and wait for it).
     template <int N>
     __device__ inline void issue_states(const T *__restrict__ q, const T *__restrict__ ref,
                                         const T *__restrict__ phi, int64_t fstride, int64_t nelem,
-                                        int local0, int step) {
+                                        int64_t own0, int local0, int step) {
         constexpr int Np = (N + 1) * (N + 1) * (N + 1);
 #pragma unroll
         for (int end = 0; end < 2; ++end) {
-            if (nb[end] >= 0 && nb[end] < nelem) {
-                const int64_t g = (int64_t)nb[end] * Np + local0 + (end == 0 ? N : 0) * step;
+            const bool valid = nb[end] >= 0 && nb[end] < nelem;
+            const int64_t e0 = valid ? (int64_t)((uint64_t)(uint32_t)nb[end] * (uint64_t)Np) : own0;
+            const int64_t g = e0 + local0 + (end == 0 ? N : 0) * step;
 #pragma unroll
-                for (int f = 0; f < 5; ++f) v[end][f] = q[f * fstride + g];
-                v[end][5] = phi[g];
-                if constexpr (PERT) {
-                    v[end][6] = ref[g];
-                    v[end][7] = ref[fstride + g];
-                }
+            for (int f = 0; f < 5; ++f) v[end][f] = q[f * fstride + g];
+            v[end][5] = phi[g];
+            if constexpr (PERT) {
+                v[end][6] = ref[g];
+                v[end][7] = ref[fstride + g];
             }
         }
     }
@@ -1413,7 +1426,8 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         constexpr int H = Nq / 2;
         FaceLoad1<T, PERT> face;
         if constexpr (SURF) {
-            if (active) face.issue_neighbour(nbr, batch * C::EPB + L.eb, L.k, L.half);
+            const int64_t e = batch * C::EPB + L.eb;  // in bounds for idle lanes (unused)
+            face.issue_neighbour(nbr, e < nelem ? e : nelem - 1, L.k, L.half);
         }
         NodeLoads<T, N, C, PERT> ld;
         ld.template issue<!SURF>(q, ref, phi, geom, fstride, B);
@@ -1460,33 +1474,52 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
         return;
     } else {
     FaceLoads<T, PERT> face;
+    // The lane's element within the batch, clamped to the batch's last one
+    // for idle lanes, and its first node: a uniform base plus a 32-bit offset.
+    const int own_eb = L.eb < B.nvalid / S::Np ? L.eb : B.nvalid / S::Np - 1;
+    const int64_t own0 = B.g0 + own_eb * S::Np;
     if constexpr (SURF) {
-        if (active) face.issue_neighbours(nbr, batch * C::EPB + L.eb, L.k);
+        // Every lane loads its neighbour indices, an idle lane those of the
+        // last element (in bounds; unused): loaded under a branch, the
+        // indices were moved between registers at the branch's end, which
+        // made each wave wait for them before issuing its node loads.
+        face.issue_neighbours(nbr + 6 * batch * C::EPB, own_eb, L.k);
+        // keep the index loads first in the queue: the partner loads wait for
+        // them, not for the node loads issued after them
+        asm volatile("" ::: "memory");
     }
     NodeLoads<T, N, C, PERT, PSPLIT> ld;
     ld.template issue<!SURF>(q, ref, phi, geom, fstride, B);
+    // Issued unconditionally, the loads may not sink towards their uses
+    // (behind the later loads): keep the issue order.
+    asm volatile("" ::: "memory");
+    // The remaining phase-A loads are issued by every lane, an idle lane
+    // reading its clamped element's values (in bounds, unused), so that the
+    // compiler can count them past the node values' wait.
     T P = T(0);  // the element's reference pressure (PSPLIT)
-    if constexpr (PSPLIT) {
-        if (active) P = ref[fstride + B.g0 + L.eb * S::Np + kPressureNode<N>];
-    }
+    if constexpr (PSPLIT) P = ref[fstride + own0 + kPressureNode<N>];
     T lm[C::kMetricInLds ? 1 : Nq][3];
     if constexpr (!C::kMetricInLds) {
-        if (active) {
-            // the line's Ja^k_1 at its first node: one 64-bit product per lane,
-            // then uniform field offsets and a pointer step along the line
-            const T *p = geom + ((int64_t)(3 * L.k) * fstride + (B.g0 + L.node_base()));
-            const int step = L.node_step();
+        // the line's Ja^k_1 at its first node, then uniform field offsets and
+        // a pointer step along the line.  3k fstride for k in {0, 1, 2} is
+        // formed with masks: the expansion of a 64-bit product reads an
+        // undefined high half, which the compiler may place in a register a
+        // node load is still writing, and then waits for that load.
+        const int64_t f3 = 3 * fstride;
+        const int64_t koff = (f3 & -(int64_t)(L.k >= 1)) + (f3 & -(int64_t)(L.k >= 2));
+        const T *p = geom + (koff + own0 + L.first_in_element());
+        const int step = L.node_step();
 #pragma unroll
-            for (int a = 0; a < Nq; ++a) {
+        for (int a = 0; a < Nq; ++a) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) lm[a][j] = p[j * fstride];
-                p += step;
-            }
+            for (int j = 0; j < 3; ++j) lm[a][j] = p[j * fstride];
+            p += step;
         }
     }
     if constexpr (SURF) {
-        if (active) face.template issue_states<N>(q, ref, phi, fstride, nelem,
-                                                     L.first_in_element(), L.node_step());
+        asm volatile("" ::: "memory");
+        face.template issue_states<N>(q, ref, phi, fstride, nelem, own0, L.first_in_element(),
+                                      L.node_step());
     }
     T mJ[S::kNodeIters];
     stage_nodes<T, N, C, PERT, PSPLIT>(ld, B, lds, mJ);

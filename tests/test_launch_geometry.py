@@ -95,6 +95,11 @@ def test_indices_in_bounds(dtype, N, nelem):
         for t in range(NT):
             for it in range(node_iters):
                 tt = t + it * NT
+                # every lane loads, one past the batch's nodes the last one
+                gl = g0 + min(tt, nvalid - 1)
+                assert 0 <= gl and 9 * fstride + gl < 10 * fstride
+                pnode = (N // 2) * (1 + Nq + Nq2)
+                assert fstride + g0 + (min(tt, nvalid - 1) // Np) * Np + pnode < 2 * fstride
                 if tt >= nvalid:
                     continue
                 g = g0 + tt
@@ -113,6 +118,17 @@ def test_indices_in_bounds(dtype, N, nelem):
             base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
             step = [1, Nq, Nq2][k]
             active = task < task_threads and eb * Np < nvalid
+            # phase A loads every lane issues, an idle lane for its element
+            # clamped to the batch's last one: the line metric and (fp32 on
+            # perturbation variables) the element's reference pressure
+            own = blk * EPB + min(eb, nvalid // Np - 1)
+            if not metric_in_lds:
+                for a in range(Nq):
+                    for j in range(3):
+                        gm = (3 * k + j) * fstride + own * Np + base + a * step
+                        assert 0 <= gm < 9 * fstride
+            pnode = (N // 2) * (1 + Nq + Nq2)
+            assert 0 <= fstride + own * Np + pnode < 2 * fstride
             if not active:
                 continue
             nb = eb * Np + base
@@ -165,11 +181,21 @@ def test_face_partner_indices(dtype, N, K, periodic):
         nvalid = min(EPB, nelem - blk * EPB) * Np
         for task in range(NT):
             eb, k, line, task_threads = line_task(task, EPB, Nq2, kmajor)
-            if not (task < task_threads and eb * Np < nvalid):
-                continue
             p1, p2 = line % Nq, line // Nq
             base = [Nq * (p1 + Nq * p2), p1 + Nq2 * p2, p1 + Nq * p2][k]
             step = [1, Nq, Nq2][k]
+            # every lane loads its neighbour indices and both partner nodes,
+            # an idle lane for its element clamped to the batch's last one, a wall or
+            # an invalid index from the lane's own element (in bounds, unused)
+            own_e = blk * EPB + min(eb, nvalid // Np - 1)
+            assert 0 <= 6 * own_e + 2 * k and 6 * own_e + 2 * k + 1 < 6 * nelem
+            for end in (0, 1):
+                nbe = nbr[own_e, 2 * k + end]
+                src = nbe if 0 <= nbe < nelem else own_e
+                g = src * Np + base + (N if end == 0 else 0) * step
+                assert 0 <= g < nelem * Np
+            if not (task < task_threads and eb * Np < nvalid):
+                continue
             e = blk * EPB + eb
             assert 0 <= 6 * e + 2 * k + 1 < 6 * nelem
             for end in (0, 1):
