@@ -1480,7 +1480,7 @@ volume_rhs_kernel(const T *__restrict__ q, const T *__restrict__ ref, const T *_
     const int64_t own0 = B.g0 + own_eb * S::Np;
     if constexpr (SURF) {
         // Every lane loads its neighbour indices, an idle lane those of the
-        // last element (in bounds; unused): loaded under a branch, the
+        // batch's last element (in bounds; unused): loaded under a branch, the
         // indices were moved between registers at the branch's end, which
         // made each wave wait for them before issuing its node loads.
         face.issue_neighbours(nbr + 6 * batch * C::EPB, own_eb, L.k);
